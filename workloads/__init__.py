@@ -1,0 +1,236 @@
+"""Seeded synthetic inputs for the paged quantized KV-cache data path.
+
+This module serves both the CPU oracle and the HIP library, and therefore
+holds none of the method's arithmetic: only random numbers (numpy PCG64 with
+a fixed seed per workload), index tables (block tables, cumulative sequence
+lengths, slot maps), random sentinel bytes for every buffer an op writes, and
+the binary32 -> bf16 input cast (round-to-nearest-even, done by torch on the
+CPU).
+
+Shapes follow the pages' workloads: the DeepSeek-V3.2 indexer K cache of the
+gather PRs (one 128-wide fp8 key row plus a 4-byte scale per token, 64-token
+pages) and the NVFP4 K/V store of vLLM's nvfp4 KV-cache kernel source (bf16
+[tokens, heads, head_size], 16-token pages).  The serving benchmark on the
+integration PR used 256 requests x 1000 prompt tokens; that shape is the
+prefill batch here.  No dataset item is reproduced; values are N(0, 1).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+INDEXER_SCALE_BYTES = 4  # one binary32 scale per token
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """binary32 -> bf16 (RNE) as uint16 bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def random_bytes(g: np.random.Generator, shape) -> np.ndarray:
+    return g.integers(0, 256, size=shape, dtype=np.uint8)
+
+
+def slots_from_table(table: np.ndarray, lens, block_size: int) -> np.ndarray:
+    """Slot of token i of request r = table[r][i // B] * B + i % B, in token order."""
+    out = []
+    for r, n in enumerate(lens):
+        i = np.arange(n, dtype=np.int64)
+        out.append(table[r, i // block_size].astype(np.int64) * block_size + i % block_size)
+    return np.concatenate(out) if out else np.zeros(0, np.int64)
+
+
+def _pages_table(g, lens, block_size, num_blocks, width=None, poison=None):
+    """Distinct pages for every request from one seeded permutation; unused
+    entries hold `poison` (a page id that no request owns) or 0."""
+    need = [(-(-n // block_size)) for n in lens]
+    width = width if width is not None else max(need + [1])
+    perm = g.permutation(num_blocks).astype(np.int32)
+    assert sum(need) <= num_blocks - (1 if poison is not None else 0)
+    fill = -1 if poison is None else poison
+    table = np.full((len(lens), width), fill, dtype=np.int32)
+    pos = 0
+    for r, n in enumerate(need):
+        table[r, :n] = perm[pos:pos + n]
+        pos += n
+    if poison is None:
+        # pad with a page that exists; the gather never reads past the
+        # request's own columns, so any in-range id is fine
+        table[table < 0] = perm[-1]
+    return table, perm
+
+
+@dataclass
+class IndexerWorkload:
+    """Indexer K cache workload: fp8 store of K, then gather back."""
+    name: str
+    block_size: int
+    head_dim: int
+    num_blocks: int
+    lens: list
+    cu_seq_lens: np.ndarray          # int32 [R+1]
+    block_table: np.ndarray          # int32 [R, maxb]
+    k_bits: np.ndarray               # uint16 [T, D] bf16 patterns, token order
+    slot_mapping: np.ndarray         # int64 [T]
+    cache_init: np.ndarray           # uint8 [num_blocks, page_bytes] sentinel bytes
+    k_fp8_init: np.ndarray           # uint8 [T + guard, D] sentinel bytes
+    k_scale_init: np.ndarray         # uint8 [T + guard, 4] sentinel bytes
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def page_bytes(self) -> int:
+        return self.block_size * (self.head_dim + INDEXER_SCALE_BYTES)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.cu_seq_lens[-1] - self.cu_seq_lens[0])
+
+
+def _indexer(name, seed, lens, block_size, head_dim, num_blocks, width=None,
+             poison=False, outlier_frac=0.0, outlier_mult=20.0, guard=3,
+             drop_frac=0.0, k_override=None):
+    g = rng(seed)
+    lens = [int(x) for x in lens]
+    poison_id = None
+    if poison:
+        poison_id = int(num_blocks - 1)
+    if poison_id is not None:
+        # keep the poison page out of the permutation's assigned prefix
+        table, _ = _pages_table(g, lens, block_size, num_blocks - 1, width, poison_id)
+    else:
+        table, _ = _pages_table(g, lens, block_size, num_blocks, width)
+    cu = np.zeros(len(lens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens, dtype=np.int64).astype(np.int32)
+    T = int(cu[-1])
+    if k_override is not None:
+        kf = k_override
+    else:
+        kf = g.standard_normal((T, head_dim), dtype=np.float32)
+        if outlier_frac > 0:
+            n_out = int(round(outlier_frac * T))
+            rows = g.choice(T, size=n_out, replace=False)
+            kf[rows] *= np.float32(outlier_mult)
+    k_bits = bf16_bits(kf)
+    slots = slots_from_table(table, lens, block_size)
+    if drop_frac > 0:
+        n_drop = int(np.floor(drop_frac * T))
+        slots[g.choice(T, size=n_drop, replace=False)] = -1
+    page_bytes = block_size * (head_dim + INDEXER_SCALE_BYTES)
+    cache = random_bytes(g, (num_blocks, page_bytes))
+    k_fp8 = random_bytes(g, (T + guard, head_dim))
+    k_scale = random_bytes(g, (T + guard, INDEXER_SCALE_BYTES))
+    return IndexerWorkload(name, block_size, head_dim, num_blocks, lens, cu, table,
+                           k_bits, slots, cache, k_fp8, k_scale,
+                           notes={"poison_page": poison_id, "seed": seed})
+
+
+def c1_tiny_gather() -> IndexerWorkload:
+    """2 requests (17 and 40 tokens), B=64, D=128, 8 pages."""
+    return _indexer("tiny_gather_2req", 1000, [17, 40], 64, 128, 8, width=4)
+
+
+def c2_prefill_256x1000() -> IndexerWorkload:
+    """256 requests x 1000 tokens, B=64, D=128, 4096 pages, 1% outlier rows x20."""
+    return _indexer("prefill_256x1000", 1001, [1000] * 256, 64, 128, 4096, width=16,
+                    outlier_frac=0.01)
+
+
+def c3_long_ragged() -> IndexerWorkload:
+    """8 requests, lengths uniform in [1, 32768], 8192 pages, block table width 512,
+    unused block-table entries hold a poison page id."""
+    lens = rng(2002).integers(1, 32769, size=8)
+    return _indexer("long_ragged_8req", 1002, lens, 64, 128, 8192, width=512,
+                    poison=True)
+
+
+def c4_roundtrip() -> IndexerWorkload:
+    """16 requests x 512 tokens stored into a 256-page cache (5% of slots = -1),
+    then gathered back."""
+    return _indexer("roundtrip_16x512", 1003, [512] * 16, 64, 128, 256, width=8,
+                    drop_frac=0.05)
+
+
+def small_indexer(seed, lens, block_size=64, head_dim=128, num_blocks=None, width=None,
+                  drop_frac=0.0, poison=False):
+    """Small random case for the property tests."""
+    need = sum(-(-int(n) // block_size) for n in lens)
+    if num_blocks is None:
+        num_blocks = max(need + 2, 4)
+    return _indexer(f"small_{seed}", seed, lens, block_size, head_dim, num_blocks,
+                    width=width, drop_frac=drop_frac, poison=poison)
+
+
+@dataclass
+class Fp4Workload:
+    """NVFP4 K/V store workload."""
+    name: str
+    num_heads: int
+    head_size: int
+    block_size: int
+    num_blocks: int
+    layout: int                      # 0 = HND, 1 = NHD
+    key_bits: np.ndarray             # uint16 [T, H*D]
+    value_bits: np.ndarray           # uint16 [T, H*D]
+    slot_mapping: np.ndarray         # int64 [T]
+    k_scale: float
+    v_scale: float
+    cache_init: np.ndarray           # uint8 [num_blocks, 2, side_bytes]
+
+    @property
+    def side_bytes(self) -> int:
+        return self.num_heads * self.block_size * (self.head_size // 2 + self.head_size // 16)
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.slot_mapping.shape[0])
+
+
+def _fp4(name, seed, T, H, D, B, num_blocks, layout=0, slots=None, drop_frac=0.05,
+         lens=None):
+    g = rng(seed)
+    if lens is not None:
+        table, _ = _pages_table(g, lens, B, num_blocks)
+        slot_mapping = slots_from_table(table, lens, B)
+        T = slot_mapping.shape[0]
+    elif slots is None:
+        slot_mapping = g.permutation(num_blocks * B)[:T].astype(np.int64)
+    else:
+        slot_mapping = np.asarray(slots, np.int64)
+    if drop_frac > 0:
+        n_drop = int(np.floor(drop_frac * T))
+        slot_mapping[g.choice(T, size=n_drop, replace=False)] = -1
+    kf = g.standard_normal((T, H * D), dtype=np.float32)
+    vf = g.standard_normal((T, H * D), dtype=np.float32)
+    k_scale, v_scale = (float(np.float32(v)) for v in g.uniform(0.5, 2.0, size=2))
+    side = H * B * (D // 2 + D // 16)
+    cache = random_bytes(g, (num_blocks, 2, side))
+    return Fp4Workload(name, H, D, B, num_blocks, layout, bf16_bits(kf), bf16_bits(vf),
+                       slot_mapping, k_scale, v_scale, cache)
+
+
+def c5_nvfp4_store(layout=0) -> Fp4Workload:
+    """K and V [4096, 8, 128], B=16, 512 pages, 5% of slots = -1, scales in [0.5, 2]."""
+    return _fp4("nvfp4_4096x8x128", 1004, 4096, 8, 128, 16, 512, layout=layout)
+
+
+def small_fp4(seed, T, H=2, D=64, B=8, num_blocks=None, layout=0, drop_frac=0.1):
+    if num_blocks is None:
+        num_blocks = max(-(-T // B) + 2, 2)
+    return _fp4(f"small_fp4_{seed}", seed, T, H, D, B, num_blocks, layout=layout,
+                drop_frac=drop_frac)
+
+
+def prefill_fp4(num_reqs=256, req_len=1000, H=8, D=128, B=16, seed=1005) -> Fp4Workload:
+    """The 256 x 1000-token prefill batch through the NVFP4 K/V store
+    (H=8, D=128, B=16); every request owns whole pages from a seeded shuffle."""
+    need = num_reqs * (-(-req_len // B))
+    num_blocks = 1 << int(np.ceil(np.log2(need)))
+    return _fp4(f"prefill_fp4_{num_reqs}x{req_len}", seed, None, H, D, B, num_blocks,
+                lens=[req_len] * num_reqs, drop_frac=0.0)
