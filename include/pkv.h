@@ -1,0 +1,185 @@
+/*
+ * pkv.h -- C ABI of libpkv, the paged quantized KV-cache data path for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Three operations, named after the pages that define them:
+ *
+ *   pkv_store_indexer_k_fp8   quantize bf16 keys per token to OCP fp8 E4M3
+ *                             with a binary32 scale (amax/448) and scatter
+ *                             codes and scale into indexer K cache pages by
+ *                             slot_mapping.
+ *   pkv_gather_indexer_k_fp8  copy the fp8 key rows and their 4 scale bytes
+ *                             of every request's tokens out of the paged
+ *                             indexer K cache into contiguous buffers, driven
+ *                             by block_table and cu_seq_lens (vLLM PR "Add
+ *                             gather_indexer_k_quant_cache kernel", call site
+ *                             with kv_cache, k_fp8, k_scale, block_table,
+ *                             cu_seq_lens; vLLM PR "[Deepseek-V3.2][Kernel]
+ *                             Integrate cuda indexer k cache gather": k_scale
+ *                             is a byte buffer viewed as float32).
+ *   pkv_store_kv_fp4          NVFP4 K/V store: 16-element blocks quantized to
+ *                             packed E2M1 plus one E4M3 block scale, written
+ *                             into [K_data|K_scale|V_data|V_scale] pages (vLLM
+ *                             source nvfp4_kv_cache_kernels.cu: header
+ *                             comment, swizzle_scale_offset,
+ *                             reshape_and_cache_nvfp4_kernel and
+ *                             reshape_and_cache_nvfp4_dispatch).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every buffer pointer is a DEVICE pointer owned by the caller.  The
+ *    library allocates nothing, never synchronizes, and enqueues its kernels
+ *    on `stream` (a hipStream_t passed as void*; NULL = the null stream).
+ *  - Inputs are read-only (const); only the documented outputs are written.
+ *  - Return value: PKV_OK (0) when the work was enqueued, or a negative
+ *    PKV_E* code, in which case NOTHING was enqueued and pkv_last_error()
+ *    returns a message (thread-local, valid until the next call on the same
+ *    thread).  Argument checks run on the host before any HIP call.
+ *  - Values that live in device memory (slots, page ids, cumulative lengths)
+ *    cannot be checked on the host without a synchronization.  Out-of-range
+ *    ones are skipped by the kernels, never dereferenced: a negative slot, a
+ *    slot past num_blocks*block_size, a page id outside [0, num_blocks), a
+ *    block-table column >= max_blocks_per_req, an output row outside
+ *    [0, num_tokens).  Duplicate slots, or overlapping cu_seq_lens ranges,
+ *    give unspecified (but in-bounds) results.
+ *  - Numerics are defined for finite bf16 inputs; non-finite inputs give
+ *    unspecified codes (memory access is unaffected).
+ *  - Results are bit-exact and independent of the launch configuration.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL (-1)        /* null pointer with non-zero work, bad size   */
+#define PKV_EUNSUPPORTED (-2)  /* valid request outside what the kernels do  */
+#define PKV_EALIGN (-3)        /* pointer or stride misaligned               */
+#define PKV_ELAUNCH (-4)       /* the HIP launch itself reported an error    */
+
+#define PKV_LAYOUT_HND 0       /* per page side: data [H][B][D/2], scales [H][B][D/16] */
+#define PKV_LAYOUT_NHD 1       /* per page side: data [B][H][D/2], scales [B][H][D/16] */
+
+/* ABI version of this header; bumped when a signature changes. */
+#define PKV_ABI_VERSION 1
+int pkv_abi_version(void);
+
+/* Message for the last non-zero status on this thread ("" if none). */
+const char *pkv_last_error(void);
+
+/*
+ * Gather (vLLM PR "Add gather_indexer_k_quant_cache kernel").
+ *
+ * For each request r in [0, num_reqs) and each token i in
+ * [0, cu_seq_lens[r+1] - cu_seq_lens[r]):
+ *     page = block_table[r * max_blocks_per_req + i / block_size]
+ *     off  = i % block_size
+ *     row  = cu_seq_lens[r] + i
+ *     k_fp8[row, 0:head_dim] = page bytes [off*head_dim, (off+1)*head_dim)
+ *     k_scale[row, 0:4]      = page bytes [block_size*head_dim + off*4, +4)
+ * Bytes are copied verbatim; no other output byte is written.
+ *
+ *   kv_cache           [num_blocks, cache_block_stride] bytes; page p starts
+ *                      at kv_cache + p*cache_block_stride and holds
+ *                      [block_size*head_dim code bytes | block_size*4 scale
+ *                      bytes].  16-byte aligned; stride a multiple of 16 and
+ *                      >= block_size*(head_dim+4).
+ *   k_fp8              [num_tokens, head_dim] bytes, written.  16-byte aligned.
+ *   k_scale            [num_tokens, 4] bytes (binary32 little-endian), written.
+ *                      4-byte aligned.
+ *   block_table        int32 [num_reqs, max_blocks_per_req], row-major.
+ *   cu_seq_lens        int32 [num_reqs + 1]; cu_seq_lens[0] need not be 0.
+ *   head_dim           multiple of 16.
+ * Errors: PKV_EINVAL for negative sizes or missing pointers, PKV_EALIGN,
+ * PKV_EUNSUPPORTED when head_dim % 16 != 0 or the stride is too small.
+ */
+int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_scale,
+                             const int32_t *block_table, const int32_t *cu_seq_lens,
+                             int32_t num_reqs, int32_t max_blocks_per_req,
+                             int64_t num_tokens, int64_t num_blocks,
+                             int64_t cache_block_stride, int32_t block_size,
+                             int32_t head_dim, void *stream);
+
+/*
+ * fp8 per-token store into the indexer K cache (the producer of the pages
+ * the gather reads; page layout as above).
+ *
+ * For each token t with slot = slot_mapping[t] >= 0 and
+ * page = slot / block_size < num_blocks, off = slot % block_size:
+ *     x_i  = bf16 k[t*k_row_stride + i], i < head_dim
+ *     s    = binary32(max_i |x_i| / 448)              (IEEE division, RNE)
+ *     code = E4M3(binary32(x_i / s))   (x_i itself when s == 0; OCP E4M3FN,
+ *                                       round to nearest even, saturating)
+ *     page bytes [off*head_dim + i]            = code_i
+ *     page bytes [block_size*head_dim + off*4, +4) = s, little-endian
+ *
+ *   k             bf16 [num_tokens, >= head_dim] with row stride k_row_stride
+ *                 ELEMENTS (>= head_dim, multiple of 8); 16-byte aligned.
+ *   slot_mapping  int64 [num_tokens]; 8-byte aligned.
+ *   kv_cache      written; 16-byte aligned; stride as for the gather.
+ *   head_dim      multiple of 16, at most 1024.
+ */
+int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride,
+                            const int64_t *slot_mapping, int64_t num_tokens,
+                            void *kv_cache, int64_t num_blocks,
+                            int64_t cache_block_stride, int32_t block_size,
+                            int32_t head_dim, void *stream);
+
+/*
+ * NVFP4 K/V store (vLLM nvfp4_kv_cache_kernels.cu).
+ *
+ * key_cache / value_cache are side 0 / side 1 of page 0 (kv_cache[:,0] and
+ * kv_cache[:,1]); page p of a side starts page_stride bytes after page p-1.
+ * Inside a side, data (H*B*D/2 bytes) is followed by scales (H*B*D/16
+ * bytes), laid out per `layout` (PKV_LAYOUT_HND or PKV_LAYOUT_NHD).
+ * For each token t with slot = slot_mapping[t] >= 0, page = slot / B <
+ * num_blocks, off = slot % B; for K then V (global scale gs = 1/k_scale,
+ * resp. 1/v_scale, binary32 division); for every head h and 16-element
+ * group g (S = D/16 groups per head):
+ *     amax = max |x|, sf = binary32(binary32(amax*gs)/6), sf8 = E4M3(sf),
+ *     r = gs / decode(sf8)  (0 when decode(sf8) == 0),
+ *     c_k = E2M1(binary32(x_k * r))  (round to nearest even, saturating at 6)
+ *     data bytes m = 0..7 of the group: c_{2m} | c_{2m+1} << 4
+ *     scale byte sf8 at (row off, column g) for K; for V at the swizzled
+ *     (row (off/4)*4 + g/(S/4), column (g % (S/4))*4 + off%4).
+ *
+ *   key, value      bf16 [num_tokens, num_heads, head_size]; heads and
+ *                   elements contiguous, token stride *_row_stride ELEMENTS
+ *                   (>= H*D, multiple of 8); 16-byte aligned.
+ *   key_cache,
+ *   value_cache     written; 8-byte aligned; page_stride multiple of 8 and
+ *                   >= the side size H*B*(D/2 + D/16).
+ *   slot_mapping    int64 [num_tokens].
+ *   k_scale,
+ *   v_scale         device binary32 scalars (the checkpoint scales).
+ *   head_size       multiple of 64 (so each 4x4 swizzle tile is complete);
+ *   block_size      multiple of 4.
+ */
+int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
+                     int64_t value_row_stride, void *key_cache, void *value_cache,
+                     const int64_t *slot_mapping, int64_t num_tokens,
+                     int32_t num_heads, int32_t head_size, int32_t block_size,
+                     int64_t num_blocks, int64_t page_stride, int32_t layout,
+                     const float *k_scale, const float *v_scale, void *stream);
+
+/*
+ * Diagnostics: the device codecs the store kernels use, exposed so that a
+ * test can sweep them over every binary32 input.
+ *   pkv_diag_encode_e4m3: out[i] = E4M3(y[i]); defined for |y[i]| < 464
+ *                         (the store kernels never pass a larger magnitude).
+ *   pkv_diag_encode_e2m1: out[i] = E2M1(y[i]) in the low nibble; defined for
+ *                         every non-NaN y[i].
+ * y: binary32 [n], 16-byte aligned; out: bytes [n]; n a multiple of 16.
+ */
+int pkv_diag_encode_e4m3(const float *y, uint8_t *out, int64_t n, void *stream);
+int pkv_diag_encode_e2m1(const float *y, uint8_t *out, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

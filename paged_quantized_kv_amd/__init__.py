@@ -1,0 +1,250 @@
+"""Python binding of libpkv (include/pkv.h): argument marshalling only.
+
+Every function takes torch tensors, checks dtypes and shapes, derives the
+sizes the C ABI needs from tensor shapes and strides, and calls the
+identically named C entry point on torch's current HIP stream.  All
+arithmetic runs in libpkv's gfx950 kernels; there is no fallback.  If
+libpkv.so is missing, importing this package raises.
+
+torch is imported before libpkv.so is loaded so that the library binds to
+the HIP runtime torch already holds (one runtime per process).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
+    "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "PkvError", "LAYOUT_HND", "LAYOUT_NHD",
+    "library_path", "abi_version",
+]
+
+LAYOUT_HND = 0
+LAYOUT_NHD = 1
+SCALE_BYTES = 4
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
+
+
+class PkvError(RuntimeError):
+    """A libpkv entry point returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _hip_runtimes_loaded():
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return paths
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"libpkv.so not found at {_LIB_PATH}; build it with __graft_entry__.build() "
+            "or python -m paged_quantized_kv_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    runtimes = _hip_runtimes_loaded()
+    if len(runtimes) > 1:
+        raise ImportError(f"more than one HIP runtime is loaded: {sorted(runtimes)}")
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.pkv_abi_version.restype = ctypes.c_int
+    lib.pkv_last_error.restype = ctypes.c_char_p
+    lib.pkv_gather_indexer_k_fp8.argtypes = [P, P, P, P, P, i32, i32, i64, i64, i64, i32, i32, P]
+    lib.pkv_store_indexer_k_fp8.argtypes = [P, i64, P, i64, P, i64, i64, i32, i32, P]
+    lib.pkv_store_kv_fp4.argtypes = [P, i64, P, i64, P, P, P, i64, i32, i32, i32, i64, i64, i32,
+                                     P, P, P]
+    lib.pkv_diag_encode_e4m3.argtypes = [P, P, i64, P]
+    lib.pkv_diag_encode_e2m1.argtypes = [P, P, i64, P]
+    for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
+                 "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load()
+
+
+def abi_version() -> int:
+    return _lib.pkv_abi_version()
+
+
+def _check(status: int):
+    if status != 0:
+        raise PkvError(status, _lib.pkv_last_error().decode(errors="replace"))
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device (cuda/HIP) tensor, got {t.device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def pkv_gather_indexer_k_fp8(kv_cache, k_fp8, k_scale, block_table, cu_seq_lens,
+                             block_size: int | None = None, stream=None):
+    """Gather fp8 key rows and their scales (vLLM cp_gather_indexer_k_quant_cache).
+
+    kv_cache:   uint8, first dim num_blocks, page = [B*D codes | B*4 scale bytes]
+                contiguous within a page (stride(0) = page stride in bytes).
+                A 3-D [num_blocks, B, D+4] view supplies block_size itself.
+    k_fp8:      uint8 (or float8_e4m3fn) [num_tokens, D], written.
+    k_scale:    uint8 [num_tokens, 4] or float32 [num_tokens] / [num_tokens, 1], written.
+    block_table int32 [num_reqs, max_blocks_per_req], cu_seq_lens int32 [num_reqs + 1].
+    """
+    _dev(kv_cache, "kv_cache", torch.uint8)
+    _dev(k_fp8, "k_fp8")
+    if k_fp8.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise TypeError("k_fp8 must be uint8 or float8_e4m3fn")
+    _dev(k_scale, "k_scale")
+    _dev(block_table, "block_table", torch.int32)
+    _dev(cu_seq_lens, "cu_seq_lens", torch.int32)
+    for t, n in ((k_fp8, "k_fp8"), (k_scale, "k_scale"), (block_table, "block_table"),
+                 (cu_seq_lens, "cu_seq_lens")):
+        _contig(t, n)
+    if k_fp8.dim() != 2:
+        raise ValueError("k_fp8 must be [num_tokens, head_dim]")
+    num_tokens, head_dim = k_fp8.shape
+    if k_scale.dtype == torch.uint8:
+        ok = k_scale.dim() == 2 and tuple(k_scale.shape) == (num_tokens, SCALE_BYTES)
+    elif k_scale.dtype == torch.float32:
+        ok = k_scale.numel() == num_tokens
+    else:
+        ok = False
+    if not ok:
+        raise ValueError("k_scale must be uint8 [num_tokens, 4] or float32 [num_tokens]")
+    if block_table.dim() != 2 or cu_seq_lens.dim() != 1:
+        raise ValueError("block_table must be 2-D and cu_seq_lens 1-D")
+    num_reqs, max_blocks = block_table.shape
+    if cu_seq_lens.numel() != num_reqs + 1:
+        raise ValueError(f"cu_seq_lens must have num_reqs + 1 = {num_reqs + 1} entries")
+    if block_size is None:
+        if kv_cache.dim() != 3:
+            raise ValueError("pass block_size, or kv_cache as [num_blocks, block_size, D + 4]")
+        block_size = kv_cache.shape[1]
+    if kv_cache.dim() >= 2 and kv_cache.stride(-1) != 1:
+        raise ValueError("kv_cache pages must be contiguous")
+    _check(_lib.pkv_gather_indexer_k_fp8(
+        kv_cache.data_ptr(), k_fp8.data_ptr(), k_scale.data_ptr(), block_table.data_ptr(),
+        cu_seq_lens.data_ptr(), num_reqs, max_blocks, num_tokens,
+        kv_cache.shape[0], kv_cache.stride(0), block_size, head_dim, _stream(stream)))
+
+
+def pkv_store_indexer_k_fp8(k, slot_mapping, kv_cache, block_size: int | None = None,
+                            stream=None):
+    """fp8 per-token quantize of bf16 k [num_tokens, D] and scatter into kv_cache."""
+    _dev(k, "k", torch.bfloat16)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(kv_cache, "kv_cache", torch.uint8)
+    _contig(slot_mapping, "slot_mapping")
+    if k.dim() != 2 or k.stride(1) != 1:
+        raise ValueError("k must be [num_tokens, head_dim] with unit element stride")
+    num_tokens, head_dim = k.shape
+    if slot_mapping.numel() != num_tokens:
+        raise ValueError("slot_mapping must have num_tokens entries")
+    if block_size is None:
+        if kv_cache.dim() != 3:
+            raise ValueError("pass block_size, or kv_cache as [num_blocks, block_size, D + 4]")
+        block_size = kv_cache.shape[1]
+    if kv_cache.stride(-1) != 1:
+        raise ValueError("kv_cache pages must be contiguous")
+    _check(_lib.pkv_store_indexer_k_fp8(
+        k.data_ptr(), k.stride(0), slot_mapping.data_ptr(), num_tokens, kv_cache.data_ptr(),
+        kv_cache.shape[0], kv_cache.stride(0), block_size, head_dim, _stream(stream)))
+
+
+def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
+                     block_size: int | None = None, layout: int | None = None, stream=None):
+    """NVFP4 store of bf16 key/value [num_tokens, H, D] into kv_cache[:,0] / kv_cache[:,1].
+
+    key_cache / value_cache: uint8 views of the two page sides.  A 4-D
+    [num_blocks, block_size, num_heads, D/2 + D/16] view supplies block_size
+    and the layout from its strides (HND when stride(2) > stride(1)), as the
+    page's dispatcher does; a 2-D [num_blocks, side_bytes] view needs both
+    passed explicitly.  k_scale / v_scale: float32 device scalars.
+    """
+    _dev(key, "key", torch.bfloat16)
+    _dev(value, "value", torch.bfloat16)
+    _dev(key_cache, "key_cache", torch.uint8)
+    _dev(value_cache, "value_cache", torch.uint8)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    _dev(k_scale, "k_scale", torch.float32)
+    _dev(v_scale, "v_scale", torch.float32)
+    _contig(slot_mapping, "slot_mapping")
+    if key.dim() != 3 or value.shape != key.shape:
+        raise ValueError("key and value must both be [num_tokens, num_heads, head_size]")
+    num_tokens, num_heads, head_size = key.shape
+    for t, n in ((key, "key"), (value, "value")):
+        if t.stride(2) != 1 or t.stride(1) != head_size:
+            raise ValueError(f"{n}: heads and elements must be contiguous (only stride(0) is free)")
+    if slot_mapping.numel() != num_tokens:
+        raise ValueError("slot_mapping must have num_tokens entries")
+    if k_scale.numel() != 1 or v_scale.numel() != 1:
+        raise ValueError("k_scale and v_scale must be scalars")
+    if key_cache.dim() == 4:
+        full_dim = head_size // 2 + head_size // 16
+        if key_cache.shape[3] != full_dim or key_cache.shape[2] != num_heads:
+            raise ValueError(f"key_cache must be [num_blocks, block_size, {num_heads}, {full_dim}]")
+        if block_size is None:
+            block_size = key_cache.shape[1]
+        if layout is None:
+            layout = LAYOUT_HND if key_cache.stride(2) > key_cache.stride(1) else LAYOUT_NHD
+    elif block_size is None or layout is None:
+        raise ValueError("pass block_size and layout, or 4-D cache views")
+    if key_cache.stride(0) != value_cache.stride(0) or key_cache.shape[0] != value_cache.shape[0]:
+        raise ValueError("key_cache and value_cache must share num_blocks and page stride")
+    _check(_lib.pkv_store_kv_fp4(
+        key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0), key_cache.data_ptr(),
+        value_cache.data_ptr(), slot_mapping.data_ptr(), num_tokens, num_heads, head_size,
+        block_size, key_cache.shape[0], key_cache.stride(0), layout, k_scale.data_ptr(),
+        v_scale.data_ptr(), _stream(stream)))
+
+
+def pkv_diag_encode_e4m3(y, out, stream=None):
+    """out[i] = device E4M3 code of y[i] (defined for |y| < 464)."""
+    _contig(_dev(y, "y", torch.float32), "y")
+    _contig(_dev(out, "out", torch.uint8), "out")
+    if out.numel() != y.numel():
+        raise ValueError("out must have y.numel() bytes")
+    _check(_lib.pkv_diag_encode_e4m3(y.data_ptr(), out.data_ptr(), y.numel(), _stream(stream)))
+
+
+def pkv_diag_encode_e2m1(y, out, stream=None):
+    """out[i] = device E2M1 code of y[i] in the low nibble (every non-NaN y)."""
+    _contig(_dev(y, "y", torch.float32), "y")
+    _contig(_dev(out, "out", torch.uint8), "out")
+    if out.numel() != y.numel():
+        raise ValueError("out must have y.numel() bytes")
+    _check(_lib.pkv_diag_encode_e2m1(y.data_ptr(), out.data_ptr(), y.numel(), _stream(stream)))

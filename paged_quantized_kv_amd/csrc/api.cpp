@@ -1,0 +1,195 @@
+// C ABI of libpkv (include/pkv.h): argument validation on the host, then the
+// kernel launchers.  Every check returns before any HIP call, so a rejected
+// call enqueues nothing.  No C++ exception crosses the ABI.
+#include "pkv.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_error[0] = '\0';
+  return PKV_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int32_t log2_or_neg(int64_t v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int32_t l = 0;
+  while ((int64_t{1} << l) < v) ++l;
+  return l;
+}
+
+int launched(int hip_status, const char* op) {
+  if (hip_status != 0)
+    return fail(PKV_ELAUNCH, "%s: kernel launch failed: %s", op,
+                hipGetErrorString(static_cast<hipError_t>(hip_status)));
+  return ok();
+}
+
+// Shared checks of the indexer page geometry.
+int check_indexer_geometry(const char* op, int64_t num_blocks, int64_t stride,
+                           int32_t block_size, int32_t head_dim) {
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "%s: num_blocks must be > 0, got %lld", op, (long long)num_blocks);
+  if (block_size <= 0) return fail(PKV_EINVAL, "%s: block_size must be > 0, got %d", op, block_size);
+  if (head_dim <= 0) return fail(PKV_EINVAL, "%s: head_dim must be > 0, got %d", op, head_dim);
+  if (head_dim % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim must be a multiple of 16, got %d", op, head_dim);
+  const int64_t page = (int64_t)block_size * (head_dim + 4);
+  if (stride < page)
+    return fail(PKV_EUNSUPPORTED,
+                "%s: cache_block_stride %lld is smaller than the page, block_size*(head_dim+4) = %lld",
+                op, (long long)stride, (long long)page);
+  if (stride % 16 != 0)
+    return fail(PKV_EALIGN, "%s: cache_block_stride must be a multiple of 16, got %lld", op, (long long)stride);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_last_error(void) { return g_error; }
+
+int pkv_gather_indexer_k_fp8(const void* kv_cache, void* k_fp8, void* k_scale,
+                             const int32_t* block_table, const int32_t* cu_seq_lens,
+                             int32_t num_reqs, int32_t max_blocks_per_req, int64_t num_tokens,
+                             int64_t num_blocks, int64_t cache_block_stride, int32_t block_size,
+                             int32_t head_dim, void* stream) {
+  static const char* op = "pkv_gather_indexer_k_fp8";
+  if (num_reqs < 0) return fail(PKV_EINVAL, "%s: num_reqs must be >= 0, got %d", op, num_reqs);
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens must be >= 0, got %lld", op, (long long)num_tokens);
+  if (int rc = check_indexer_geometry(op, num_blocks, cache_block_stride, block_size, head_dim)) return rc;
+  if (max_blocks_per_req < 0)
+    return fail(PKV_EINVAL, "%s: max_blocks_per_req must be >= 0, got %d", op, max_blocks_per_req);
+  // no requests, no output rows or no page columns: nothing can be written
+  if (num_reqs == 0 || num_tokens == 0 || max_blocks_per_req == 0) return ok();
+  if ((int64_t)num_reqs * max_blocks_per_req > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req exceeds 2^31-1", op);
+  if (!kv_cache || !k_fp8 || !k_scale || !block_table || !cu_seq_lens)
+    return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(kv_cache, 16) || !aligned(k_fp8, 16))
+    return fail(PKV_EALIGN, "%s: kv_cache and k_fp8 must be 16-byte aligned", op);
+  if (!aligned(k_scale, 4) || !aligned(block_table, 4) || !aligned(cu_seq_lens, 4))
+    return fail(PKV_EALIGN, "%s: k_scale, block_table and cu_seq_lens must be 4-byte aligned", op);
+  pkv::GatherArgs a{static_cast<const uint8_t*>(kv_cache), static_cast<uint8_t*>(k_fp8),
+                    static_cast<uint8_t*>(k_scale), block_table, cu_seq_lens, num_reqs,
+                    max_blocks_per_req, num_tokens, num_blocks, cache_block_stride, block_size,
+                    head_dim};
+  return launched(pkv::launch_gather_indexer_k_fp8(a, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_store_indexer_k_fp8(const void* k, int64_t k_row_stride, const int64_t* slot_mapping,
+                            int64_t num_tokens, void* kv_cache, int64_t num_blocks,
+                            int64_t cache_block_stride, int32_t block_size, int32_t head_dim,
+                            void* stream) {
+  static const char* op = "pkv_store_indexer_k_fp8";
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens must be >= 0, got %lld", op, (long long)num_tokens);
+  if (int rc = check_indexer_geometry(op, num_blocks, cache_block_stride, block_size, head_dim)) return rc;
+  if (head_dim > 1024) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be <= 1024, got %d", op, head_dim);
+  if (k_row_stride < head_dim)
+    return fail(PKV_EINVAL, "%s: k_row_stride %lld < head_dim %d", op, (long long)k_row_stride, head_dim);
+  if (k_row_stride % 8 != 0)
+    return fail(PKV_EALIGN, "%s: k_row_stride must be a multiple of 8 elements, got %lld", op, (long long)k_row_stride);
+  if (num_tokens == 0) return ok();
+  if (!k || !slot_mapping || !kv_cache) return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(k, 16) || !aligned(kv_cache, 16))
+    return fail(PKV_EALIGN, "%s: k and kv_cache must be 16-byte aligned", op);
+  if (!aligned(slot_mapping, 8)) return fail(PKV_EALIGN, "%s: slot_mapping must be 8-byte aligned", op);
+  if (num_tokens > ((int64_t)1 << 40)) return fail(PKV_EUNSUPPORTED, "%s: num_tokens too large", op);
+  pkv::StoreFp8Args a{static_cast<const uint16_t*>(k), k_row_stride, slot_mapping, num_tokens,
+                      static_cast<uint8_t*>(kv_cache), num_blocks, cache_block_stride, block_size,
+                      log2_or_neg(block_size), head_dim};
+  return launched(pkv::launch_store_indexer_k_fp8(a, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,
+                     int64_t value_row_stride, void* key_cache, void* value_cache,
+                     const int64_t* slot_mapping, int64_t num_tokens, int32_t num_heads,
+                     int32_t head_size, int32_t block_size, int64_t num_blocks, int64_t page_stride,
+                     int32_t layout, const float* k_scale, const float* v_scale, void* stream) {
+  static const char* op = "pkv_store_kv_fp4";
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens must be >= 0, got %lld", op, (long long)num_tokens);
+  if (num_heads <= 0) return fail(PKV_EINVAL, "%s: num_heads must be > 0, got %d", op, num_heads);
+  if (head_size <= 0) return fail(PKV_EINVAL, "%s: head_size must be > 0, got %d", op, head_size);
+  if (block_size <= 0) return fail(PKV_EINVAL, "%s: block_size must be > 0, got %d", op, block_size);
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "%s: num_blocks must be > 0, got %lld", op, (long long)num_blocks);
+  // The page's own checks (head_size % 16, block_size % 4), plus head_size %
+  // 64 so that every 4x4 swizzle tile of the V scales is complete.
+  if (head_size % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: head_size must be divisible by 16 for NVFP4 KV cache, got %d", op, head_size);
+  if (head_size % 64 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: head_size must be a multiple of 64 for the V-scale swizzle, got %d", op, head_size);
+  if (block_size % 4 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size must be divisible by 4 for the NVFP4 swizzle, got %d", op, block_size);
+  if (layout != PKV_LAYOUT_HND && layout != PKV_LAYOUT_NHD)
+    return fail(PKV_EINVAL, "%s: layout must be PKV_LAYOUT_HND or PKV_LAYOUT_NHD, got %d", op, layout);
+  const int64_t hd = (int64_t)num_heads * head_size;
+  if (hd > ((int64_t)1 << 24)) return fail(PKV_EUNSUPPORTED, "%s: num_heads*head_size too large", op);
+  if (key_row_stride < hd || value_row_stride < hd)
+    return fail(PKV_EINVAL, "%s: row strides must be >= num_heads*head_size = %lld", op, (long long)hd);
+  if (key_row_stride % 8 != 0 || value_row_stride % 8 != 0)
+    return fail(PKV_EALIGN, "%s: row strides must be multiples of 8 elements", op);
+  const int64_t side = (int64_t)num_heads * block_size * (head_size / 2 + head_size / 16);
+  if (page_stride < side)
+    return fail(PKV_EUNSUPPORTED, "%s: page_stride %lld is smaller than one side, %lld bytes", op,
+                (long long)page_stride, (long long)side);
+  if (page_stride % 8 != 0) return fail(PKV_EALIGN, "%s: page_stride must be a multiple of 8", op);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !key_cache || !value_cache || !slot_mapping || !k_scale || !v_scale)
+    return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(key, 16) || !aligned(value, 16))
+    return fail(PKV_EALIGN, "%s: key and value must be 16-byte aligned", op);
+  if (!aligned(key_cache, 8) || !aligned(value_cache, 8) || !aligned(slot_mapping, 8))
+    return fail(PKV_EALIGN, "%s: caches and slot_mapping must be 8-byte aligned", op);
+  if (!aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return fail(PKV_EALIGN, "%s: k_scale and v_scale must be 4-byte aligned", op);
+  pkv::StoreFp4Args a{static_cast<const uint16_t*>(key), key_row_stride,
+                      static_cast<const uint16_t*>(value), value_row_stride,
+                      static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache),
+                      slot_mapping, num_tokens, num_heads, head_size, block_size,
+                      log2_or_neg(block_size), num_blocks, page_stride, layout, k_scale, v_scale};
+  return launched(pkv::launch_store_kv_fp4(a, static_cast<hipStream_t>(stream)), op);
+}
+
+static int check_diag(const char* op, const float* y, const uint8_t* out, int64_t n) {
+  if (n < 0 || n % 16 != 0) return fail(PKV_EINVAL, "%s: n must be a non-negative multiple of 16", op);
+  if (n > 0 && (!y || !out)) return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(y, 16) || !aligned(out, 16)) return fail(PKV_EALIGN, "%s: buffers must be 16-byte aligned", op);
+  return PKV_OK;
+}
+
+int pkv_diag_encode_e4m3(const float* y, uint8_t* out, int64_t n, void* stream) {
+  static const char* op = "pkv_diag_encode_e4m3";
+  if (int rc = check_diag(op, y, out, n)) return rc;
+  if (n == 0) return ok();
+  return launched(pkv::launch_diag_e4m3(y, out, n, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_diag_encode_e2m1(const float* y, uint8_t* out, int64_t n, void* stream) {
+  static const char* op = "pkv_diag_encode_e2m1";
+  if (int rc = check_diag(op, y, out, n)) return rc;
+  if (n == 0) return ok();
+  return launched(pkv::launch_diag_e2m1(y, out, n, static_cast<hipStream_t>(stream)), op);
+}
+
+}  // extern "C"

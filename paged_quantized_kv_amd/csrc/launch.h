@@ -1,0 +1,73 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel
+// launchers.  Launchers assume validated arguments and return 0 or the HIP
+// error code of the launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// One workgroup stages cu_seq_lens and the run prefix of up to this many
+// requests in LDS (4 bytes each, under 64 KiB with the static scratch);
+// larger tables are launched in
+// request chunks.
+constexpr int64_t kGatherMaxReqsPerLaunch = 16000;
+constexpr int64_t kGatherMaxBlocks = 65536;
+constexpr int64_t kFp4MaxBlocks = 8192;
+
+struct GatherArgs {
+  const uint8_t* kv_cache;
+  uint8_t* k_fp8;
+  uint8_t* k_scale;
+  const int32_t* block_table;
+  const int32_t* cu_seq_lens;
+  int32_t num_reqs;
+  int32_t max_blocks_per_req;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int64_t cache_block_stride;
+  int32_t block_size;
+  int32_t head_dim;
+};
+
+struct StoreFp8Args {
+  const uint16_t* k;
+  int64_t k_row_stride;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  uint8_t* kv_cache;
+  int64_t num_blocks;
+  int64_t cache_block_stride;
+  int32_t block_size;
+  int32_t log2_block_size;  // -1 when block_size is not a power of two
+  int32_t head_dim;
+};
+
+struct StoreFp4Args {
+  const uint16_t* key;
+  int64_t key_row_stride;
+  const uint16_t* value;
+  int64_t value_row_stride;
+  uint8_t* key_cache;
+  uint8_t* value_cache;
+  const int64_t* slot_mapping;
+  int64_t num_tokens;
+  int32_t num_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int32_t log2_block_size;
+  int64_t num_blocks;
+  int64_t page_stride;
+  int32_t layout;
+  const float* k_scale;
+  const float* v_scale;
+};
+
+int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream);
+int launch_store_indexer_k_fp8(const StoreFp8Args& a, hipStream_t stream);
+int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream);
+int launch_diag_e4m3(const float* y, uint8_t* out, int64_t n, hipStream_t stream);
+int launch_diag_e2m1(const float* y, uint8_t* out, int64_t n, hipStream_t stream);
+
+}  // namespace pkv

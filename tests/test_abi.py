@@ -1,0 +1,152 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/pkv.h declares, and its host-side validation rejects bad arguments
+(and accepts empty work) before any HIP call is made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+import paged_quantized_kv_amd as pkv  # noqa: E402
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EALIGN = 0, -1, -2, -3
+A = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(pkv_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for s in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
+              "pkv_last_error", "pkv_abi_version"):
+        assert s in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pkv.library_path())
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (pkv_\w+)$", out, re.M))
+    for s in declared_symbols():
+        assert s in exported, s
+        assert getattr(lib, s) is not None
+    assert pkv.abi_version() == 1
+
+
+def lib():
+    return pkv._lib
+
+
+def last_error():
+    return lib().pkv_last_error().decode()
+
+
+def gather(**kw):
+    a = dict(kv_cache=A, k_fp8=A, k_scale=A, block_table=A, cu=A, R=2, maxb=4, T=57, nb=8,
+             stride=64 * 132, B=64, D=128)
+    a.update(kw)
+    return lib().pkv_gather_indexer_k_fp8(a["kv_cache"], a["k_fp8"], a["k_scale"],
+                                          a["block_table"], a["cu"], a["R"], a["maxb"], a["T"],
+                                          a["nb"], a["stride"], a["B"], a["D"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=100), PKV_EUNSUPPORTED, "multiple of 16"),
+    (dict(stride=64 * 132 - 16), PKV_EUNSUPPORTED, "smaller than the page"),
+    (dict(stride=64 * 132 + 8), PKV_EALIGN, "multiple of 16"),
+    (dict(R=-1), PKV_EINVAL, "num_reqs"),
+    (dict(T=-5), PKV_EINVAL, "num_tokens"),
+    (dict(nb=0), PKV_EINVAL, "num_blocks"),
+    (dict(B=0), PKV_EINVAL, "block_size"),
+    (dict(maxb=-1), PKV_EINVAL, "max_blocks_per_req"),
+    (dict(k_fp8=0), PKV_EINVAL, "null"),
+    (dict(kv_cache=A + 4), PKV_EALIGN, "16-byte"),
+    (dict(k_scale=A + 2), PKV_EALIGN, "4-byte"),
+    (dict(R=70000, maxb=40000), PKV_EUNSUPPORTED, "2^31"),
+])
+def test_gather_validation(kw, code, msg):
+    assert gather(**kw) == code
+    assert msg in last_error()
+
+
+@pytest.mark.parametrize("kw", [dict(R=0), dict(T=0), dict(maxb=0),
+                                dict(R=0, kv_cache=0, k_fp8=0, k_scale=0)])
+def test_gather_empty_work_is_ok_without_launch(kw):
+    assert gather(**kw) == PKV_OK
+    assert last_error() == ""
+
+
+def store8(**kw):
+    a = dict(k=A, ks=128, slots=A, T=10, cache=A, nb=4, stride=64 * 132, B=64, D=128)
+    a.update(kw)
+    return lib().pkv_store_indexer_k_fp8(a["k"], a["ks"], a["slots"], a["T"], a["cache"],
+                                         a["nb"], a["stride"], a["B"], a["D"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=1040, ks=1040, stride=64 * 1044), PKV_EUNSUPPORTED),
+    (dict(D=24), PKV_EUNSUPPORTED),
+    (dict(ks=100), PKV_EINVAL),
+    (dict(ks=132), PKV_EALIGN),
+    (dict(k=A + 8), PKV_EALIGN),
+    (dict(slots=A + 4), PKV_EALIGN),
+    (dict(cache=0), PKV_EINVAL),
+    (dict(T=-1), PKV_EINVAL),
+])
+def test_store_fp8_validation(kw, code):
+    assert store8(**kw) == code
+
+
+def test_store_fp8_empty_is_ok():
+    assert store8(T=0, k=0, slots=0, cache=0) == PKV_OK
+
+
+def store4(**kw):
+    a = dict(key=A, kst=1024, val=A, vst=1024, kc=A, vc=A + 9216, slots=A, T=8, H=8, D=128,
+             B=16, nb=4, page=18432, layout=0, kscale=A, vscale=A)
+    a.update(kw)
+    return lib().pkv_store_kv_fp4(a["key"], a["kst"], a["val"], a["vst"], a["kc"], a["vc"],
+                                  a["slots"], a["T"], a["H"], a["D"], a["B"], a["nb"], a["page"],
+                                  a["layout"], a["kscale"], a["vscale"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=40, kst=320, vst=320), PKV_EUNSUPPORTED, "divisible by 16"),
+    (dict(D=96, kst=768, vst=768), PKV_EUNSUPPORTED, "multiple of 64"),
+    (dict(B=6), PKV_EUNSUPPORTED, "divisible by 4"),
+    (dict(layout=2), PKV_EINVAL, "layout"),
+    (dict(kst=1000), PKV_EINVAL, "row strides"),
+    (dict(kst=1028), PKV_EALIGN, "multiples of 8"),
+    (dict(page=9000), PKV_EUNSUPPORTED, "smaller than one side"),
+    (dict(page=9220), PKV_EALIGN, "page_stride"),
+    (dict(kscale=0), PKV_EINVAL, "null"),
+    (dict(vc=A + 4), PKV_EALIGN, "8-byte"),
+    (dict(H=0), PKV_EINVAL, "num_heads"),
+])
+def test_store_fp4_validation(kw, code, msg):
+    assert store4(**kw) == code
+    assert msg in last_error()
+
+
+def test_store_fp4_empty_is_ok():
+    assert store4(T=0, key=0, val=0, kc=0, vc=0, slots=0, kscale=0, vscale=0) == PKV_OK
+
+
+def test_diag_validation():
+    assert lib().pkv_diag_encode_e4m3(A, A, 15, None) == PKV_EINVAL
+    assert lib().pkv_diag_encode_e2m1(A + 4, A, 16, None) == PKV_EALIGN
+    assert lib().pkv_diag_encode_e4m3(0, 0, 0, None) == PKV_OK
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    x = torch.zeros(4, 128, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="device"):
+        pkv.pkv_gather_indexer_k_fp8(x, x, x, x, x, block_size=64)

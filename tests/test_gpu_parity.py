@@ -1,0 +1,366 @@
+"""GPU parity: libpkv's gfx950 kernels, called through the C ABI (via the
+Python binding), against the CPU oracle on the same seeded inputs.
+
+Every comparison is bit-exact and covers whole buffers: caches (so bytes a
+kernel must not touch are checked too) and outputs with guard rows.  Sizes
+span several tiles with ragged tails; the 256 x 1000-token prefill batch is
+compared in full for the fp8 store and the gather; the NVFP4 store at that
+scale is compared on sampled tokens the oracle recomputes one by one.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_quantized_kv_amd as pkv
+
+DEV = "cuda:0"
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def bf16_dev(bits, shape=None):
+    t = dev(bits.view(np.int16)).view(torch.bfloat16)
+    return t if shape is None else t.view(*shape)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def banner(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+# ---------------------------------------------------------------- gather
+def run_gather(w, cache_np, block_table=None, cu=None, k_rows=None):
+    bt = w.block_table if block_table is None else block_table
+    cu = w.cu_seq_lens if cu is None else cu
+    kf0 = w.k_fp8_init if k_rows is None else w.k_fp8_init[:k_rows]
+    ks0 = w.k_scale_init if k_rows is None else w.k_scale_init[:k_rows]
+    ref_f, ref_s = kf0.copy(), ks0.copy()
+    oracle.gather_indexer_k_fp8(cache_np, ref_f, ref_s, bt, cu, w.block_size, w.head_dim)
+    kf, ks = dev(kf0), dev(ks0)
+    pkv.pkv_gather_indexer_k_fp8(dev(cache_np), kf, ks, dev(bt), dev(cu),
+                                 block_size=w.block_size)
+    np.testing.assert_array_equal(host(kf), ref_f)
+    np.testing.assert_array_equal(host(ks), ref_s)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3"])
+def test_gather_configs_random_pages(name):
+    w = {"c1": workloads.c1_tiny_gather, "c3": workloads.c3_long_ragged}[name]()
+    banner(f"gather {w.name} lens={w.lens[:8]}")
+    run_gather(w, w.cache_init)
+
+
+def test_gather_prefill_256x1000_full():
+    w = workloads.c2_prefill_256x1000()
+    banner(f"gather {w.name}")
+    run_gather(w, w.cache_init)
+
+
+@pytest.mark.parametrize("lens,bs,hd", [
+    ([0, 1, 63, 64, 65, 0, 200, 129], 64, 128),
+    ([5, 9, 31, 16, 17], 16, 64),
+    ([130, 1, 255], 32, 256),
+    ([300, 7], 48, 128),          # block size that is not a power of two
+    ([1000], 64, 1024),
+    ([1] * 700, 64, 128),         # many short requests: several prefix tiles per thread
+])
+def test_gather_ragged(lens, bs, hd):
+    banner(f"gather ragged lens={lens[:6]}.. B={bs} D={hd}")
+    width = max(1, max(-(-n // bs) for n in lens)) + 3
+    w = workloads.small_indexer(len(lens) * 7 + bs + hd, lens, block_size=bs, head_dim=hd,
+                                poison=True, width=width)
+    run_gather(w, w.cache_init)
+
+
+def test_gather_skip_rules_and_offsets():
+    banner("gather skip rules")
+    w = workloads.small_indexer(77, [100, 30, 70, 5], width=3)
+    bt = w.block_table.copy()
+    bt[0, 1] = w.num_blocks + 3      # page past the cache
+    bt[1, 0] = -1                    # negative page
+    bt[2, 1] = w.num_blocks          # first invalid id
+    run_gather(w, w.cache_init, block_table=bt)
+    # cu_seq_lens not starting at 0, and rows beyond num_tokens (clipped)
+    cu = w.cu_seq_lens.copy() + 5
+    run_gather(w, w.cache_init, cu=cu, k_rows=150)
+    # a request longer than the table is wide
+    cu2 = np.array([0, 250, 250, 260, 300], np.int32)
+    run_gather(w, w.cache_init, cu=cu2, k_rows=w.k_fp8_init.shape[0])
+
+
+def test_gather_many_requests_chunked_launch():
+    lens = [1 + (i % 3) for i in range(17000)]   # more requests than one launch stages
+    banner("gather 17000 requests")
+    w = workloads.small_indexer(99, lens, block_size=16, head_dim=64, width=1)
+    run_gather(w, w.cache_init)
+
+
+def test_gather_empty():
+    banner("gather empty")
+    w = workloads.c1_tiny_gather()
+    cu = np.zeros(3, np.int32)
+    run_gather(w, w.cache_init, cu=cu)
+    kf = dev(w.k_fp8_init[:0])
+    pkv.pkv_gather_indexer_k_fp8(dev(w.cache_init), kf, dev(w.k_scale_init[:0]),
+                                 dev(w.block_table), dev(w.cu_seq_lens), block_size=64)
+
+
+# ---------------------------------------------------------------- fp8 store
+def run_store8(w, k_bits=None, slots=None, cache_np=None, row_pad=0):
+    kb = w.k_bits if k_bits is None else k_bits
+    sl = w.slot_mapping if slots is None else slots
+    c0 = w.cache_init if cache_np is None else cache_np
+    ref = c0.copy()
+    if row_pad:
+        kb = np.concatenate([kb, np.full((kb.shape[0], row_pad), 0x7F80, np.uint16)], axis=1)
+    oracle.store_indexer_k_fp8(np.ascontiguousarray(kb), sl, ref, w.block_size, w.head_dim)
+    cache = dev(c0)
+    k = bf16_dev(np.ascontiguousarray(kb))[:, :w.head_dim]
+    pkv.pkv_store_indexer_k_fp8(k, dev(sl), cache, block_size=w.block_size)
+    got = host(cache)
+    np.testing.assert_array_equal(got, ref)
+    return got
+
+
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_store_fp8_configs(name):
+    w = {"c1": workloads.c1_tiny_gather, "c4": workloads.c4_roundtrip}[name]()
+    banner(f"store fp8 {w.name}")
+    run_store8(w)
+
+
+def test_store_fp8_prefill_256x1000_full():
+    w = workloads.c2_prefill_256x1000()
+    banner(f"store fp8 {w.name}")
+    run_store8(w)
+
+
+@pytest.mark.parametrize("lens,bs,hd", [
+    ([37, 64, 1], 64, 16), ([100, 3], 16, 32), ([65, 70], 32, 64), ([200], 64, 256),
+    ([50, 51], 64, 512), ([20], 8, 1024), ([90, 33], 48, 128), ([10, 11], 64, 96),
+])
+def test_store_fp8_shapes(lens, bs, hd):
+    banner(f"store fp8 lens={lens} B={bs} D={hd}")
+    w = workloads.small_indexer(sum(lens) + hd, lens, block_size=bs, head_dim=hd, drop_frac=0.1)
+    run_store8(w)
+
+
+def test_store_fp8_row_stride_and_skips():
+    banner("store fp8 padded rows, -1 and out-of-range slots")
+    w = workloads.small_indexer(5, [300, 77], drop_frac=0.2)
+    sl = w.slot_mapping.copy()
+    sl[4] = w.num_blocks * w.block_size          # first slot past the cache
+    sl[9] = w.num_blocks * w.block_size + 1000
+    run_store8(w, slots=sl, row_pad=24)
+    run_store8(w, slots=np.full_like(sl, -1))
+
+
+def test_store_fp8_value_edge_cases():
+    """Zero, tiny (IEEE-division path), subnormal, huge and tie-making tokens."""
+    banner("store fp8 value edge cases")
+    g = workloads.rng(123)
+    T, D = 512, 128
+    x = g.standard_normal((T, D)).astype(np.float32)
+    x[0] = 0.0
+    x[1, ::2] = -0.0
+    x[1, 1::2] = 0.0
+    x[2] *= np.float32(2.0 ** -70)             # amax < 2^-60: division path
+    x[3] = np.float32(2.0 ** -133)             # smallest bf16 subnormal everywhere
+    x[3, ::3] *= -1
+    x[4] *= np.float32(2.0 ** -126)            # subnormal bf16 values
+    x[5] *= np.float32(1e37)                   # large magnitudes, still finite
+    x[6] = np.float32(3.3895314e38)
+    x[7, :] = 1.953125 * 2.0 ** -16            # W8-style ties
+    x[7, 0] = 1.953125
+    x[8:64] *= np.exp2(g.integers(-60, 60, size=(56, 1))).astype(np.float32)
+    x[64:128] *= np.float32(2.0 ** -60)        # right at the path boundary
+    # every bf16 significand as amax, paired with every bf16 significand below it
+    sig = (np.arange(128, dtype=np.uint32) | 0x3F80) << 16
+    sigf = sig.view(np.float32)
+    for i in range(128, 256):
+        row = np.tile(sigf, 1)[:D] * np.float32(2.0 ** -((i % 20)))
+        row[0] = sigf[i - 128] * np.float32(2.0 ** 3)
+        x[i] = row
+    kb = workloads.bf16_bits(x)
+    w = workloads.small_indexer(3, [T], drop_frac=0.0)
+    run_store8(w, k_bits=kb)
+
+
+def test_store_then_gather_roundtrip_c4():
+    w = workloads.c4_roundtrip()
+    banner(f"round trip {w.name}")
+    cache_ref = w.cache_init.copy()
+    oracle.store_indexer_k_fp8(w.k_bits, w.slot_mapping, cache_ref, w.block_size, w.head_dim)
+    kf_ref, ks_ref = w.k_fp8_init.copy(), w.k_scale_init.copy()
+    oracle.gather_indexer_k_fp8(cache_ref, kf_ref, ks_ref, w.block_table, w.cu_seq_lens,
+                                w.block_size, w.head_dim)
+    cache = dev(w.cache_init)
+    kf, ks = dev(w.k_fp8_init), dev(w.k_scale_init)
+    pkv.pkv_store_indexer_k_fp8(bf16_dev(w.k_bits), dev(w.slot_mapping), cache, block_size=64)
+    pkv.pkv_gather_indexer_k_fp8(cache, kf, ks, dev(w.block_table), dev(w.cu_seq_lens),
+                                 block_size=64)
+    np.testing.assert_array_equal(host(cache), cache_ref)
+    np.testing.assert_array_equal(host(kf), kf_ref)
+    np.testing.assert_array_equal(host(ks), ks_ref)
+
+
+def test_store_gather_on_side_stream():
+    banner("side stream")
+    w = workloads.c1_tiny_gather()
+    s = torch.cuda.Stream()
+    cache_ref = w.cache_init.copy()
+    oracle.store_indexer_k_fp8(w.k_bits, w.slot_mapping, cache_ref, 64, 128)
+    cache = dev(w.cache_init)
+    k, sl = bf16_dev(w.k_bits), dev(w.slot_mapping)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        pkv.pkv_store_indexer_k_fp8(k, sl, cache, block_size=64)
+    s.synchronize()
+    np.testing.assert_array_equal(cache.cpu().numpy(), cache_ref)
+
+
+# ---------------------------------------------------------------- NVFP4 store
+def run_store4(f, slots=None, layout=None, key_bits=None):
+    layout = f.layout if layout is None else layout
+    sl = f.slot_mapping if slots is None else slots
+    kb = f.key_bits if key_bits is None else key_bits
+    ref = f.cache_init.copy()
+    oracle.store_kv_fp4(kb, f.value_bits, ref, sl, f.num_heads, f.head_size, f.block_size,
+                        layout, f.k_scale, f.v_scale)
+    c = dev(f.cache_init)
+    T = sl.shape[0]
+    shape = (T, f.num_heads, f.head_size)
+    pkv.pkv_store_kv_fp4(bf16_dev(kb, shape), bf16_dev(f.value_bits, shape), c[:, 0], c[:, 1],
+                         dev(sl), torch.tensor([f.k_scale], dtype=torch.float32, device=DEV),
+                         torch.tensor([f.v_scale], dtype=torch.float32, device=DEV),
+                         block_size=f.block_size, layout=layout)
+    np.testing.assert_array_equal(host(c), ref)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_store_fp4_c5(layout):
+    f = workloads.c5_nvfp4_store(layout)
+    banner(f"nvfp4 {f.name} layout={layout}")
+    run_store4(f)
+
+
+@pytest.mark.parametrize("T,H,D,B,layout", [
+    (37, 1, 64, 4, 0), (100, 2, 128, 8, 1), (64, 3, 192, 12, 0), (50, 5, 256, 16, 1),
+    (130, 8, 128, 32, 0), (9, 16, 64, 64, 1), (33, 7, 128, 20, 0),
+])
+def test_store_fp4_shapes(T, H, D, B, layout):
+    banner(f"nvfp4 T={T} H={H} D={D} B={B} layout={layout}")
+    f = workloads.small_fp4(T * 13 + H, T, H=H, D=D, B=B, layout=layout)
+    run_store4(f)
+
+
+def test_store_fp4_value_edge_cases():
+    banner("nvfp4 value edge cases")
+    f = workloads.small_fp4(5, 64, H=2, D=128, B=16, drop_frac=0.0)
+    x = (f.key_bits.astype(np.uint32) << 16).view(np.float32).reshape(64, 2, 8, 16).copy()
+    x[0] = 0.0
+    x[1, :, :, ::2] = -0.0
+    x[2] *= np.float32(2.0 ** -120)          # block scale underflows E4M3
+    x[3] *= np.float32(2.0 ** -8)            # subnormal E4M3 block scales
+    x[4] *= np.float32(1e30)                 # block scale saturates at 448
+    x[5, :, :, 0] = 6.0                      # exact ties on the E2M1 grid
+    x[5, :, :, 1:] = np.array([2.5, .25, .75, 5, 1.25, 1.75, -.5, 3.5, 4, 1, 2, 3, .5, 1.5, -6],
+                              np.float32)
+    x[6:] *= np.exp2(np.random.default_rng(1).integers(-30, 30, size=(58, 1, 1, 1))).astype(np.float32)
+    kb = workloads.bf16_bits(x.reshape(64, -1))
+    run_store4(f, key_bits=kb)
+    run_store4(f, slots=np.full_like(f.slot_mapping, -1))
+
+
+def test_store_fp4_prefill_sampled():
+    """256 x 1000-token prefill batch, H=8, D=128, B=16 (the benchmark's shape):
+    full GPU run; the oracle recomputes 3000 sampled tokens and every byte those
+    tokens own is compared, plus the K and V scale regions of their pages."""
+    f = workloads.prefill_fp4()
+    banner(f"nvfp4 {f.name} sampled")
+    c = dev(f.cache_init)
+    T = f.num_tokens
+    shape = (T, f.num_heads, f.head_size)
+    pkv.pkv_store_kv_fp4(bf16_dev(f.key_bits, shape), bf16_dev(f.value_bits, shape), c[:, 0],
+                         c[:, 1], dev(f.slot_mapping),
+                         torch.tensor([f.k_scale], dtype=torch.float32, device=DEV),
+                         torch.tensor([f.v_scale], dtype=torch.float32, device=DEV),
+                         block_size=f.block_size, layout=f.layout)
+    got = host(c)
+    pick = np.sort(workloads.rng(5).choice(T, size=3000, replace=False))
+    ref = f.cache_init.copy()
+    oracle.store_kv_fp4(np.ascontiguousarray(f.key_bits[pick]),
+                        np.ascontiguousarray(f.value_bits[pick]), ref,
+                        np.ascontiguousarray(f.slot_mapping[pick]), f.num_heads, f.head_size,
+                        f.block_size, f.layout, f.k_scale, f.v_scale)
+    owned = ref != f.cache_init           # bytes the sampled tokens changed
+    # plus every byte they own that happens to equal the sentinel: the data rows
+    H, D, B = f.num_heads, f.head_size, f.block_size
+    for slot in f.slot_mapping[pick]:
+        p, off = divmod(int(slot), B)
+        for h in range(H):
+            a = (h * B + off) * (D // 2)
+            owned[p, :, a:a + D // 2] = True
+    assert owned.sum() > 3000 * 2 * H * D // 2
+    np.testing.assert_array_equal(got[owned], ref[owned])
+
+
+# ---------------------------------------------------------------- codecs
+def _sweep(encode, lo_bits, hi_bits, oracle_fn, chunk=1 << 26):
+    """Compare the device codec with the oracle on every binary32 pattern in
+    [lo_bits, hi_bits) (unsigned bit order)."""
+    from concurrent.futures import ThreadPoolExecutor
+    pool = ThreadPoolExecutor(16)
+    start = lo_bits
+    while start < hi_bits:
+        n = min(chunk, hi_bits - start)
+        n16 = (n + 15) // 16 * 16
+        b = torch.arange(start, start + n16, dtype=torch.int64, device=DEV)
+        b = torch.where(b < hi_bits, b, torch.full_like(b, lo_bits))
+        b = torch.where(b >= 2 ** 31, b - 2 ** 32, b).to(torch.int32)
+        y32 = b.view(torch.float32)
+        out = torch.empty(n16, dtype=torch.uint8, device=DEV)
+        encode(y32.contiguous(), out)
+        got = out.cpu().numpy()
+        ybits = np.arange(start, start + n16, dtype=np.int64)
+        ybits = np.where(ybits < hi_bits, ybits, lo_bits).astype(np.uint32)
+        yf = ybits.view(np.float32)
+        parts = np.array_split(np.arange(n16), 16)
+        ref = np.empty(n16, np.uint8)
+
+        def work(ix):
+            ref[ix] = oracle_fn(yf[ix])
+        list(pool.map(work, parts))
+        bad = np.nonzero(got != ref)[0]
+        assert bad.size == 0, (f"{bad.size} mismatches, first y=0x{ybits[bad[0]]:08x} "
+                               f"got {got[bad[0]]:#x} want {ref[bad[0]]:#x}")
+        start += n
+    pool.shutdown()
+
+
+def test_device_e4m3_codec_exhaustive_below_464():
+    banner("e4m3 codec sweep")
+    lim = int(np.array([464.0], np.float32).view(np.uint32)[0])
+    _sweep(pkv.pkv_diag_encode_e4m3, 0, lim, oracle.e4m3_encode)
+    _sweep(pkv.pkv_diag_encode_e4m3, 0x80000000, 0x80000000 + lim, oracle.e4m3_encode)
+
+
+def test_device_e2m1_codec_exhaustive():
+    banner("e2m1 codec sweep")
+    # every non-NaN pattern: [0, +inf] and [-0, -inf]
+    _sweep(pkv.pkv_diag_encode_e2m1, 0, 0x7F800001, oracle.e2m1_encode)
+    _sweep(pkv.pkv_diag_encode_e2m1, 0x80000000, 0xFF800001, oracle.e2m1_encode)
