@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Throughput of the paged quantized KV-cache data path on one MI355X.
+
+One step is one pass of the whole path over the prefill batch of 256 requests
+x 1000 tokens (the shape of the serving benchmark on the vLLM integration PR
+"[Deepseek-V3.2][Kernel] Integrate cuda indexer k cache gather"):
+
+  1. pkv_store_indexer_k_fp8  bf16 K [256000, 128] -> fp8 codes + binary32 scales
+                              into 4096 indexer pages of 64 tokens (slots from
+                              each request's block-table row);
+  2. pkv_store_kv_fp4         bf16 K and V [256000, 8, 128] -> NVFP4 pages of 16
+                              tokens, [K_data|K_scale|V_data|V_scale], HND;
+  3. pkv_gather_indexer_k_fp8 the indexer pages back into contiguous k_fp8
+                              [256000, 128] and k_scale [256000, 4], driven by
+                              block_table and cu_seq_lens.
+
+Inputs are synthetic (seeded N(0,1), 1% outlier rows x20 for the indexer K)
+and resident in HBM before timing starts.  The indexer buffers rotate over
+two sets; the NVFP4 store moves ~1.35 GB per step, far more than the 256 MB
+Infinity Cache, so every kernel reads data that has been evicted.
+
+Printed: one JSON line.  `value` = algorithmic bytes of one step / measured
+step time (GB/s); per-kernel durations come from HIP events recorded on the
+launch stream around each launch; `roofline` describes the kernel with the
+longest average duration; `cpu_baseline` times the CPU oracle on the same
+batch (one thread).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+METRIC = "gather/store HBM GB/s and % of MI355X peak; Mtokens/s at 256×1000 tok"
+
+CSRC = os.path.join(ROOT, "paged_quantized_kv_amd", "csrc")
+KERNEL_SOURCES = {
+    "store_indexer_k_fp8": ["store_indexer_k_fp8.hip", "device_common.h"],
+    "store_kv_fp4": ["store_kv_fp4.hip", "device_common.h"],
+    "gather_indexer_k_fp8": ["gather_indexer_k_fp8.hip", "device_common.h"],
+}
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current source of the kernel; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_prefill_256x1000_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_t = re.search(r"^traffic_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    m_h = re.search(r"^source_sha256:\s*([0-9a-f]+)", text, re.M)
+    if not m_t or not m_h or m_h.group(1) != source_hash(kernel):
+        return None
+    return float(m_t.group(1))
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--sets", type=int, default=2, help="rotating indexer buffer sets")
+    p.add_argument("--no-cpu-baseline", action="store_true",
+                   help="skip the CPU oracle timing (profiling runs)")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="run a plain 256 MiB fp32 copy-like kernel (torch.neg) before the "
+                        "timed steps, for scaling hardware byte counters")
+    return p.parse_args()
+
+
+def algorithmic_bytes(T, D, H4, D4, R, maxb):
+    """Bytes each op must move at minimum (read + write), per step."""
+    store8 = T * (2 * D + 8 + D + 4)                     # bf16 K + slot -> codes + scale
+    gather = T * 2 * (D + 4) + R * maxb * 4 + (R + 1) * 4  # pages -> k_fp8/k_scale, metadata
+    fp4 = T * (2 * H4 * D4 * 2 + 8 + 2 * H4 * (D4 // 2 + D4 // 16)) + 8  # K,V,slot -> pages
+    return {"store_indexer_k_fp8": store8, "store_kv_fp4": fp4, "gather_indexer_k_fp8": gather}
+
+
+def cpu_baseline(w, f, step_bytes):
+    import numpy as np
+
+    import oracle
+    cache = w.cache_init.copy()
+    kf, ks = w.k_fp8_init.copy(), w.k_scale_init.copy()
+    c4 = f.cache_init.copy()
+    t0 = time.perf_counter()
+    oracle.store_indexer_k_fp8(w.k_bits, w.slot_mapping, cache, w.block_size, w.head_dim)
+    oracle.store_kv_fp4(f.key_bits, f.value_bits, c4, f.slot_mapping, f.num_heads, f.head_size,
+                        f.block_size, f.layout, f.k_scale, f.v_scale)
+    oracle.gather_indexer_k_fp8(cache, kf, ks, w.block_table, w.cu_seq_lens, w.block_size,
+                                w.head_dim)
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "seconds": round(dt, 3),
+            "mtokens_per_s": round(w.num_tokens / dt / 1e6, 4),
+            "sample": "one full step (256 req x 1000 tok through fp8 store, NVFP4 store and "
+                      "gather), plain C oracle, one thread"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the path has "
+              "no cross-GPU step; requests and tokens shard across GPUs with no exchange)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_quantized_kv_amd as pkv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    w = workloads.c2_prefill_256x1000()
+    f = workloads.prefill_fp4()
+    T, D = w.num_tokens, w.head_dim
+    R, maxb = w.block_table.shape
+    H4, D4 = f.num_heads, f.head_size
+    assert f.num_tokens == T
+    t_gen = time.perf_counter() - t_gen
+
+    def to(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    sets = []
+    for _ in range(args.sets):
+        sets.append({
+            "k": to(w.k_bits.view(np.int16)).view(torch.bfloat16),
+            "slot": to(w.slot_mapping),
+            "cache": to(w.cache_init),
+            "kf": to(w.k_fp8_init[:T]),
+            "ks": to(w.k_scale_init[:T]),
+        })
+    bt, cu = to(w.block_table), to(w.cu_seq_lens)
+    key = to(f.key_bits.view(np.int16)).view(torch.bfloat16).view(T, H4, D4)
+    val = to(f.value_bits.view(np.int16)).view(torch.bfloat16).view(T, H4, D4)
+    slot4 = to(f.slot_mapping)
+    c4 = to(f.cache_init)
+    k4s = torch.tensor([f.k_scale], dtype=torch.float32, device=dev)
+    v4s = torch.tensor([f.v_scale], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    names = ["store_indexer_k_fp8", "store_kv_fp4", "gather_indexer_k_fp8"]
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        pkv.pkv_store_indexer_k_fp8(s["k"], s["slot"], s["cache"], block_size=w.block_size)
+        if ev is not None:
+            ev[1].record()
+        pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slot4, k4s, v4s,
+                             block_size=f.block_size, layout=f.layout)
+        if ev is not None:
+            ev[2].record()
+        pkv.pkv_gather_indexer_k_fp8(s["cache"], s["kf"], s["ks"], bt, cu,
+                                     block_size=w.block_size)
+        if ev is not None:
+            ev[3].record()
+
+    if args.calibration_copy:
+        src = torch.randn(64 << 20, device=dev)          # 256 MiB fp32
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # Events are created before the warmup so that no host-side pause separates
+    # the warmup from the timed steps (an idle GPU lowers its clocks).
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = {n: 0.0 for n in names}
+    for ev in events:
+        for j, n in enumerate(names):
+            per_kernel_ms[n] += ev[j].elapsed_time(ev[j + 1])
+    per_kernel_ms = {n: v / args.steps for n, v in per_kernel_ms.items()}
+    ms_per_step = wall * 1e3 / args.steps
+
+    alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
+    step_bytes = sum(alg.values())
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    kernels = {}
+    for n in names:
+        ms = per_kernel_ms[n]
+        gbps = alg[n] / (ms * 1e-3) / 1e9
+        kernels[n] = {"us": round(ms * 1e3, 2), "alg_bytes": alg[n], "GBps": round(gbps, 1),
+                      "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+                      "mtokens_per_s": round(T / (ms * 1e-3) / 1e6, 1)}
+    dom = max(names, key=lambda n: per_kernel_ms[n])
+    dom_gbps = kernels[dom]["GBps"]
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dom),
+                "alg_bytes_per_launch": alg[dom]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill batch 256 req x 1000 tok: indexer K fp8 store + gather "
+                        "(D=128, B=64, 4096 pages) and NVFP4 K/V store (H=8, D=128, B=16, HND)",
+            "tokens": T,
+            "requests": R,
+            "parallelism": "single GPU",
+        },
+        "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "mtokens_per_s": round(T / (ms_per_step * 1e-3) / 1e6, 2),
+        "event_ms_per_step": round(sum(per_kernel_ms.values()), 4),
+        "kernels": kernels,
+        "roofline": roofline,
+        "input_gen_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, f, step_bytes)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

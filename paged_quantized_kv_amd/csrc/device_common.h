@@ -111,6 +111,17 @@ __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
 __device__ __forceinline__ u32x4 load_stream(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_stream(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (workgroup b runs on
+// XCD b % 8).  Renumbering b so that each XCD receives one contiguous range
+// of logical blocks keeps neighbouring work items -- e.g. the tokens that
+// share a cache page -- in one XCD's L2, where their partial-line writes
+// merge.  A bijection on [0, gridDim.x) when gridDim.x is a multiple of 8.
+constexpr uint32_t kNumXcd = 8;
+__device__ __forceinline__ uint32_t xcd_contiguous_block() {
+  const uint32_t b = blockIdx.x;
+  return (b % kNumXcd) * (gridDim.x / kNumXcd) + b / kNumXcd;
+}
+
 // slot -> (page, offset) for a block size that may or may not be a power of two.
 __device__ __forceinline__ void split_slot(int64_t slot, int32_t block_size, int32_t log2_bs,
                                            int64_t& page, int64_t& off) {

@@ -11,11 +11,15 @@
 // 16-byte loads and stores (8 per lane for a 64 x 128-byte run), then the
 // scale dwords, one per lane.
 //
-// Run index -> (request, column): every workgroup builds the exclusive
-// prefix sum of runs per request, min(ceil(len_r / block_size),
-// max_blocks_per_req), in LDS from cu_seq_lens, and each wave finds its
-// request by binary search.  Waves stride over runs until all are done, so
-// the grid size only sets parallelism, never coverage.
+// Which wave copies which run:
+//  - dense tables (at most about twice as many entries as page runs): wave w
+//    takes block-table entry (w / max_blocks, w % max_blocks) and exits at
+//    once if that column holds no tokens;
+//  - otherwise every workgroup builds the exclusive prefix sum of runs per
+//    request, min(ceil(len_r / block_size), max_blocks_per_req), in LDS from
+//    cu_seq_lens, and each wave finds its request by binary search.
+// In both, waves stride over the work until all of it is done, so the grid
+// size only sets parallelism, never coverage.
 #include "device_common.h"
 #include "launch.h"
 
@@ -26,6 +30,83 @@ namespace {
 constexpr int kGatherThreads = 256;
 constexpr int kGatherWaves = kGatherThreads / kWave;
 constexpr int kGatherUnroll = 8;  // 16-byte chunks per lane in flight
+
+// Copy page run j of a request whose rows are [start, end) of the output:
+// tokens [j*B, min((j+1)*B, len)) of the request, all in page `page`
+// starting at offset 0.  Rows outside [0, num_tokens) and pages outside
+// [0, num_blocks) are skipped.  Executed by one whole wave.
+__device__ __forceinline__ void copy_run(const uint8_t* __restrict__ kv_cache,
+                                         uint8_t* __restrict__ k_fp8,
+                                         uint8_t* __restrict__ k_scale, int64_t start,
+                                         int64_t end, int64_t page, int32_t j,
+                                         int64_t num_tokens, int64_t num_blocks,
+                                         int64_t page_stride, int32_t block_size,
+                                         int32_t head_dim, int lane) {
+  const int64_t len = end - start;
+  if (page < 0 || page >= num_blocks) return;
+  const int64_t i0 = (int64_t)j * block_size;
+  if (i0 >= len) return;
+  const int64_t n = (len - i0 < block_size) ? (len - i0) : block_size;
+  const int64_t row0 = start + i0;
+  const int64_t rb = row0 > 0 ? row0 : 0;
+  const int64_t re = (row0 + n < num_tokens) ? row0 + n : num_tokens;
+  if (rb >= re) return;
+
+  const uint8_t* src = kv_cache + page * page_stride;
+  const int64_t first = rb - row0;  // first page offset copied
+  const int64_t rows = re - rb;
+
+  // scale dwords (issued first; at most block_size of them)
+  const uint32_t* ssrc =
+      reinterpret_cast<const uint32_t*>(src + (int64_t)block_size * head_dim) + first;
+  uint32_t* sdst = reinterpret_cast<uint32_t*>(k_scale) + rb;
+  uint32_t sv = 0;
+  const bool has_scale = lane < rows;
+  if (has_scale) sv = ssrc[lane];
+
+  // code rows: one contiguous span of rows*head_dim bytes
+  const u32x4* csrc = reinterpret_cast<const u32x4*>(src + first * head_dim);
+  u32x4* cdst = reinterpret_cast<u32x4*>(k_fp8 + rb * head_dim);
+  const int64_t chunks = rows * head_dim / 16;
+  for (int64_t c0 = 0; c0 < chunks; c0 += kWave * kGatherUnroll) {
+    u32x4 v[kGatherUnroll];
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int64_t c = c0 + u * kWave + lane;
+      if (c < chunks) v[u] = load_stream(csrc + c);
+    }
+#pragma unroll
+    for (int u = 0; u < kGatherUnroll; ++u) {
+      const int64_t c = c0 + u * kWave + lane;
+      if (c < chunks) store_stream(cdst + c, v[u]);
+    }
+  }
+  if (has_scale) sdst[lane] = sv;
+  for (int64_t c = lane + kWave; c < rows; c += kWave) sdst[c] = ssrc[c];
+}
+
+// Dense tables: wave w copies block-table entry (r, j) = (w / max_blocks,
+// w % max_blocks) when that column holds tokens of request r.  The three
+// metadata loads are independent, so a wave reaches its data after one
+// round trip.  Used when the table has at most about twice as many entries
+// as there can be page runs.
+__global__ __launch_bounds__(kGatherThreads) void gather_indexer_k_fp8_direct_kernel(
+    const uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ k_fp8,
+    uint8_t* __restrict__ k_scale, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ cu_seq_lens, int32_t num_reqs, int32_t max_blocks,
+    int64_t num_tokens, int64_t num_blocks, int64_t page_stride, int32_t block_size,
+    int32_t head_dim) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t entries = (int64_t)num_reqs * max_blocks;
+  const int64_t stride = (int64_t)gridDim.x * kGatherWaves;
+  for (int64_t w = (int64_t)blockIdx.x * kGatherWaves + threadIdx.x / kWave; w < entries;
+       w += stride) {
+    const int32_t r = (int32_t)(w / max_blocks);
+    const int32_t j = (int32_t)(w - (int64_t)r * max_blocks);
+    copy_run(kv_cache, k_fp8, k_scale, cu_seq_lens[r], cu_seq_lens[r + 1], block_table[w], j,
+             num_tokens, num_blocks, page_stride, block_size, head_dim, lane);
+  }
+}
 
 __global__ __launch_bounds__(kGatherThreads) void gather_indexer_k_fp8_kernel(
     const uint8_t* __restrict__ kv_cache, uint8_t* __restrict__ k_fp8,
@@ -89,64 +170,42 @@ __global__ __launch_bounds__(kGatherThreads) void gather_indexer_k_fp8_kernel(
     const int32_t r = lo;
     const int32_t j = run - run_start[r];
 
-    const int64_t start = cu_seq_lens[r];
-    const int64_t len = (int64_t)cu_seq_lens[r + 1] - start;
-    const int64_t page = block_table[(int64_t)r * max_blocks + j];
-    if (page < 0 || page >= num_blocks) continue;
-
-    const int64_t i0 = (int64_t)j * block_size;
-    const int64_t n = (len - i0 < block_size) ? (len - i0) : block_size;
-    const int64_t row0 = start + i0;
-    const int64_t rb = row0 > 0 ? row0 : 0;
-    const int64_t re = (row0 + n < num_tokens) ? row0 + n : num_tokens;
-    if (rb >= re) continue;
-
-    const uint8_t* src = kv_cache + page * page_stride;
-    const int64_t first = rb - row0;  // first page offset copied
-    const int64_t rows = re - rb;
-
-    // scale dwords (issued first; at most block_size of them)
-    const uint32_t* ssrc = reinterpret_cast<const uint32_t*>(src + (int64_t)block_size * head_dim) + first;
-    uint32_t* sdst = reinterpret_cast<uint32_t*>(k_scale) + rb;
-    uint32_t sv = 0;
-    const bool has_scale = lane < rows;
-    if (has_scale) sv = ssrc[lane];
-
-    // code rows: one contiguous span of rows*head_dim bytes
-    const u32x4* csrc = reinterpret_cast<const u32x4*>(src + first * head_dim);
-    u32x4* cdst = reinterpret_cast<u32x4*>(k_fp8 + rb * head_dim);
-    const int64_t chunks = rows * head_dim / 16;
-    for (int64_t c0 = 0; c0 < chunks; c0 += kWave * kGatherUnroll) {
-      u32x4 v[kGatherUnroll];
-#pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) {
-        const int64_t c = c0 + u * kWave + lane;
-        if (c < chunks) v[u] = load_stream(csrc + c);
-      }
-#pragma unroll
-      for (int u = 0; u < kGatherUnroll; ++u) {
-        const int64_t c = c0 + u * kWave + lane;
-        if (c < chunks) store_stream(cdst + c, v[u]);
-      }
-    }
-    if (has_scale) sdst[lane] = sv;
-    for (int64_t c = lane + kWave; c < rows; c += kWave) sdst[c] = ssrc[c];
+    copy_run(kv_cache, k_fp8, k_scale, cu_seq_lens[r], cu_seq_lens[r + 1],
+             block_table[(int64_t)r * max_blocks + j], j, num_tokens, num_blocks, page_stride,
+             block_size, head_dim, lane);
   }
 }
 
 }  // namespace
 
+#ifndef PKV_GATHER_MODE
+#define PKV_GATHER_MODE 0  // 0: choose per call, 1: always prefix scan, 2: always direct
+#endif
+
 int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream) {
+  // Upper bound on page runs when the rows fit num_tokens: sum(len)/B + R.
+  const int64_t table = (int64_t)a.num_reqs * a.max_blocks_per_req;
+  const int64_t run_bound = (a.num_tokens + a.block_size - 1) / a.block_size + a.num_reqs;
+  const bool direct = PKV_GATHER_MODE == 2 || (PKV_GATHER_MODE == 0 && table <= 2 * run_bound);
+  if (direct) {
+    int64_t blocks = (table + kGatherWaves - 1) / kGatherWaves;
+    if (blocks > kGatherMaxBlocks) blocks = kGatherMaxBlocks;
+    hipLaunchKernelGGL(gather_indexer_k_fp8_direct_kernel, dim3((unsigned)blocks),
+                       dim3(kGatherThreads), 0, stream, a.kv_cache, a.k_fp8, a.k_scale,
+                       a.block_table, a.cu_seq_lens, a.num_reqs, a.max_blocks_per_req,
+                       a.num_tokens, a.num_blocks, a.cache_block_stride, a.block_size,
+                       a.head_dim);
+    return (int)hipGetLastError();
+  }
   // Requests are independent, so a table with more requests than one
   // workgroup's LDS prefix array can hold is processed in request chunks.
   const int64_t max_chunk = kGatherMaxReqsPerLaunch;
   for (int64_t r0 = 0; r0 < a.num_reqs; r0 += max_chunk) {
     const int32_t R = (int32_t)((a.num_reqs - r0) < max_chunk ? (a.num_reqs - r0) : max_chunk);
-    // Upper bound on runs when the rows fit num_tokens: sum(len)/B + R.
-    // More runs are still all copied (grid-stride loop).
+    // More runs than this bound are still all copied (grid-stride loop).
     int64_t bound = (a.num_tokens + a.block_size - 1) / a.block_size + R;
-    const int64_t table = (int64_t)R * a.max_blocks_per_req;
-    if (table < bound) bound = table;
+    const int64_t chunk_table = (int64_t)R * a.max_blocks_per_req;
+    if (chunk_table < bound) bound = chunk_table;
     int64_t blocks = (bound + kGatherWaves - 1) / kGatherWaves;
     if (blocks < 1) blocks = 1;
     if (blocks > kGatherMaxBlocks) blocks = kGatherMaxBlocks;

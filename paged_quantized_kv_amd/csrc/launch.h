@@ -14,7 +14,10 @@ namespace pkv {
 // request chunks.
 constexpr int64_t kGatherMaxReqsPerLaunch = 16000;
 constexpr int64_t kGatherMaxBlocks = 65536;
-constexpr int64_t kFp4MaxBlocks = 8192;
+#ifndef PKV_FP4_MAX_BLOCKS
+#define PKV_FP4_MAX_BLOCKS 65536
+#endif
+constexpr int64_t kFp4MaxBlocks = PKV_FP4_MAX_BLOCKS;
 
 struct GatherArgs {
   const uint8_t* kv_cache;

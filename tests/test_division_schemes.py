@@ -1,0 +1,69 @@
+"""Exhaustive host-side checks that the division shortcuts the HIP kernels
+use give the IEEE binary32 quotient.
+
+The kernels replace some correctly rounded divisions with Markstein's
+correction step (P. Markstein, IBM J. Res. Dev. 34(1), 1990): with rs =
+RN(1/s), q0 = RN(x*rs), e = fma(-q0, s, x) (exact), q1 = RN(q0 + e*rs).  The
+result scales exactly by powers of two while no step leaves the normal
+range, so checking every significand pair covers every exponent the kernels
+let through.  Two uses are checked here, each over its whole domain:
+  * the fp8 store: x a bf16 value (128 significands), s = RN(amax/448) for
+    any binary32 significand (2^23), i.e. 2^30 pairs;
+  * the NVFP4 block scale: t/6 for every binary32 significand t (2^23).
+The program is plain C compiled with gcc (hardware fma when the host has
+it, glibc's correctly rounded fmaf otherwise)."""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+SRC = r"""
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+static float f_of(uint32_t b) { float f; memcpy(&f, &b, 4); return f; }
+static uint32_t b_of(float f) { uint32_t b; memcpy(&b, &f, 4); return b; }
+static float markstein(float x, float s, float rs) {
+  float q0 = x * rs;
+  float e = fmaf(-q0, s, x);
+  return fmaf(e, rs, q0);
+}
+int main(void) {
+  long bad6 = 0, bad8 = 0;
+  volatile float six = 6.0f;
+  float r6 = 1.0f / six;
+  for (uint32_t m = 0; m < (1u << 23); ++m) {
+    float t = f_of(0x3F800000u | m);                  /* t in [1, 2) */
+    if (b_of(markstein(t, six, r6)) != b_of(t / six)) ++bad6;
+  }
+  for (uint32_t ms = 0; ms < (1u << 23); ++ms) {
+    float s = f_of(0x3F800000u | ms);                 /* s in [1, 2) */
+    float rs = 1.0f / s;
+    for (uint32_t mx = 0; mx < 128; ++mx) {
+      float x = f_of(0x3F800000u | (mx << 16));       /* bf16 significand */
+      if (b_of(markstein(x, s, rs)) != b_of(x / s)) ++bad8;
+      float x2 = x * 2.0f;                            /* quotient in [1, 4) */
+      if (b_of(markstein(x2, s, rs)) != b_of(x2 / s)) ++bad8;
+    }
+  }
+  printf("%ld %ld\n", bad6, bad8);
+  return 0;
+}
+"""
+
+
+def test_markstein_quotients_equal_ieee_division():
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "m.c")
+        exe = os.path.join(d, "m")
+        open(c, "w").write(SRC)
+        flags = ["-O2", "-std=c11", "-fno-fast-math", "-ffp-contract=off"]
+        if "fma" in open("/proc/cpuinfo").read().split():
+            flags.append("-mfma")
+        subprocess.run(["gcc", *flags, c, "-o", exe, "-lm"], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True, timeout=600)
+    bad6, bad8 = map(int, out.stdout.split())
+    assert bad6 == 0, f"{bad6} significands where the corrected t/6 differs"
+    assert bad8 == 0, f"{bad8} significand pairs where the corrected x/s differs"

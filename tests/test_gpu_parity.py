@@ -364,3 +364,50 @@ def test_device_e2m1_codec_exhaustive():
     # every non-NaN pattern: [0, +inf] and [-0, -inf]
     _sweep(pkv.pkv_diag_encode_e2m1, 0, 0x7F800001, oracle.e2m1_encode)
     _sweep(pkv.pkv_diag_encode_e2m1, 0x80000000, 0xFF800001, oracle.e2m1_encode)
+
+
+def _fp4_custom(x_key, x_val, B, k_scale, v_scale, seed=9):
+    """NVFP4 workload around caller-chosen K/V values [T, H, D] (one page per 4 tokens)."""
+    T, H, D = x_key.shape
+    g = workloads.rng(seed)
+    nb = -(-T // B) + 1
+    f = workloads.Fp4Workload(
+        "custom", H, D, B, nb, 0, workloads.bf16_bits(x_key.reshape(T, -1)),
+        workloads.bf16_bits(x_val.reshape(T, -1)), np.arange(T, dtype=np.int64),
+        float(np.float32(k_scale)), float(np.float32(v_scale)),
+        workloads.random_bytes(g, (nb, 2, H * B * (D // 2 + D // 16))))
+    return f
+
+
+def test_store_fp4_every_block_scale_code():
+    """k_scale = v_scale = 1 and block amax = 6 * decode(c): the block scale is
+    exactly decode(c), so every E4M3 code 0..126 appears as a block scale (and
+    every entry of the reciprocal table with every exponent is used)."""
+    banner("nvfp4 every block-scale code")
+    codes = np.arange(127, dtype=np.uint8)
+    dec = oracle.e4m3_decode(codes).astype(np.float32)
+    H, D, B = 2, 64, 4                      # 4 blocks per head, 16 blocks per token
+    nblk = 2 * H * (D // 16)
+    T = -(-len(codes) // nblk) + 1
+    g = workloads.rng(17)
+    blocks = np.zeros((T * nblk, 16), np.float32)
+    for i, c in enumerate(codes):
+        amax = np.float32(6.0) * dec[c]
+        frac = g.uniform(-1, 1, 15).astype(np.float32)
+        blocks[i, 0] = amax if i % 2 else -amax
+        blocks[i, 1:] = frac * amax
+    x = blocks.reshape(T, 2, H, D)
+    f = _fp4_custom(x[:, 0].copy(), x[:, 1].copy(), B, 1.0, 1.0)
+    run_store4(f)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** 110, 2.0 ** -110])
+def test_store_fp4_global_scale_outside_table_range(scale):
+    banner(f"nvfp4 k_scale = {scale:g}")
+    g = workloads.rng(23)
+    T, H, D, B = 24, 2, 128, 8
+    mag = np.float32(2.0 ** 100 if scale > 1 else 2.0 ** -100)
+    x = (g.standard_normal((T, H, D)) * mag).astype(np.float32)
+    y = g.standard_normal((T, H, D)).astype(np.float32)
+    f = _fp4_custom(x, y, B, scale, 1.0)
+    run_store4(f)

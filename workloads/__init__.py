@@ -16,6 +16,8 @@ prefill batch here.  No dataset item is reproduced; values are N(0, 1).
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -26,6 +28,31 @@ INDEXER_SCALE_BYTES = 4  # one binary32 scale per token
 
 def rng(seed: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(seed))
+
+
+_CHUNK = 1 << 22
+
+
+def normal_f32(g: np.random.Generator, shape) -> np.ndarray:
+    """N(0, 1) binary32 array.  Large arrays are drawn in fixed 4 Mi-element
+    chunks, chunk i from PCG64(SeedSequence([base, i])) with base drawn from
+    g, on a thread pool; the values do not depend on the thread count."""
+    n = int(np.prod(shape))
+    if n <= _CHUNK:
+        return g.standard_normal(shape, dtype=np.float32)
+    base = int(g.integers(0, 2 ** 63))
+    out = np.empty(n, dtype=np.float32)
+    starts = range(0, n, _CHUNK)
+
+    def fill(i_start):
+        i, start = i_start
+        gen = np.random.Generator(np.random.PCG64(np.random.SeedSequence([base, i])))
+        gen.standard_normal(min(_CHUNK, n - start), dtype=np.float32,
+                            out=out[start:start + _CHUNK])
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(fill, enumerate(starts)))
+    return out.reshape(shape)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -112,7 +139,7 @@ def _indexer(name, seed, lens, block_size, head_dim, num_blocks, width=None,
     if k_override is not None:
         kf = k_override
     else:
-        kf = g.standard_normal((T, head_dim), dtype=np.float32)
+        kf = normal_f32(g, (T, head_dim))
         if outlier_frac > 0:
             n_out = int(round(outlier_frac * T))
             rows = g.choice(T, size=n_out, replace=False)
@@ -206,8 +233,8 @@ def _fp4(name, seed, T, H, D, B, num_blocks, layout=0, slots=None, drop_frac=0.0
     if drop_frac > 0:
         n_drop = int(np.floor(drop_frac * T))
         slot_mapping[g.choice(T, size=n_drop, replace=False)] = -1
-    kf = g.standard_normal((T, H * D), dtype=np.float32)
-    vf = g.standard_normal((T, H * D), dtype=np.float32)
+    kf = normal_f32(g, (T, H * D))
+    vf = normal_f32(g, (T, H * D))
     k_scale, v_scale = (float(np.float32(v)) for v in g.uniform(0.5, 2.0, size=2))
     side = H * B * (D // 2 + D // 16)
     cache = random_bytes(g, (num_blocks, 2, side))
