@@ -76,8 +76,8 @@ def measured_traffic(kernel: str):
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--sets", type=int, default=2, help="rotating indexer buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
@@ -192,7 +192,10 @@ def main():
         del src, dst
 
     # Events are created before the warmup so that no host-side pause separates
-    # the warmup from the timed steps (an idle GPU lowers its clocks).
+    # the warmup from the timed steps (an idle GPU lowers its clocks).  The
+    # default warmup (~30 ms of steps) runs past the clock transient that the
+    # first few dozen launches of the step show, so the timed steps measure the
+    # sustained rate.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.warmup):
         step(i)
