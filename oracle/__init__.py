@@ -50,6 +50,8 @@ def _load():
                               ctypes.c_uint8, ctypes.c_uint16)
     lib.oracle_bf16_to_f32.argtypes = [u16]
     lib.oracle_bf16_to_f32.restype = f32
+    lib.oracle_f16_to_f32.argtypes = [u16]
+    lib.oracle_f16_to_f32.restype = f32
     lib.oracle_e4m3_encode.argtypes = [f32]
     lib.oracle_e4m3_encode.restype = u8
     lib.oracle_e4m3_decode.argtypes = [u8]
@@ -67,9 +69,9 @@ def _load():
     lib.oracle_gather_indexer_k_fp8.argtypes = [P, P, P, P, P, i32, i32, i64, i64,
                                                 i64, i32, i32]
     lib.oracle_gather_indexer_k_fp8.restype = None
-    lib.oracle_store_indexer_k_fp8.argtypes = [P, i64, P, i64, P, i64, i64, i32, i32]
+    lib.oracle_store_indexer_k_fp8.argtypes = [P, i64, i32, P, i64, P, i64, i64, i32, i32]
     lib.oracle_store_indexer_k_fp8.restype = None
-    lib.oracle_store_kv_fp4.argtypes = [P, i64, P, i64, P, P, P, i64, i32, i32, i32,
+    lib.oracle_store_kv_fp4.argtypes = [P, i64, P, i64, i32, P, P, P, i64, i32, i32, i32,
                                         i64, i64, i32, f32, f32]
     lib.oracle_store_kv_fp4.restype = None
     _lib = lib
@@ -144,15 +146,26 @@ def gather_indexer_k_fp8(kv_cache, k_fp8, k_scale, block_table, cu_seq_lens,
         kv_cache.shape[1], block_size, head_dim)
 
 
-def store_indexer_k_fp8(k_bits, slot_mapping, kv_cache, block_size, head_dim):
-    """Quantize bf16 rows (uint16 bit patterns [T, >=D]) into kv_cache (in place)."""
+SRC_DTYPES = {"bf16": 0, "f16": 1}
+
+
+def f16_to_f32(bits) -> np.ndarray:
+    lib = _load()
+    bits = np.asarray(bits, dtype=np.uint16)
+    return np.array([lib.oracle_f16_to_f32(int(b)) for b in bits.ravel()],
+                    dtype=np.float32).reshape(bits.shape)
+
+
+def store_indexer_k_fp8(k_bits, slot_mapping, kv_cache, block_size, head_dim, dtype="bf16"):
+    """Quantize 16-bit float rows (uint16 bit patterns [T, >=D], bf16 or f16)
+    into kv_cache (in place)."""
     _need(k_bits, np.uint16, "k_bits")
     _need(slot_mapping, np.int64, "slot_mapping")
     _need(kv_cache, np.uint8, "kv_cache")
     assert k_bits.ndim == 2 and k_bits.shape[1] >= head_dim
     assert slot_mapping.shape == (k_bits.shape[0],)
     _load().oracle_store_indexer_k_fp8(
-        _ptr(k_bits), k_bits.shape[1], _ptr(slot_mapping), k_bits.shape[0],
+        _ptr(k_bits), k_bits.shape[1], SRC_DTYPES[dtype], _ptr(slot_mapping), k_bits.shape[0],
         _ptr(kv_cache), kv_cache.shape[0], kv_cache.shape[1], block_size, head_dim)
 
 
@@ -161,8 +174,8 @@ LAYOUT_NHD = 1
 
 
 def store_kv_fp4(key_bits, value_bits, kv_cache, slot_mapping, num_heads, head_size,
-                 block_size, layout, k_scale, v_scale):
-    """NVFP4 store of bf16 K/V (uint16 patterns [T, H*D]) into kv_cache (in place).
+                 block_size, layout, k_scale, v_scale, dtype="bf16"):
+    """NVFP4 store of bf16 or f16 K/V (uint16 patterns [T, H*D]) into kv_cache (in place).
 
     kv_cache: uint8 [num_blocks, 2, side_bytes]; side 0 holds K, side 1 holds V.
     """
@@ -178,6 +191,6 @@ def store_kv_fp4(key_bits, value_bits, kv_cache, slot_mapping, num_heads, head_s
     page_stride = 2 * side_bytes
     _load().oracle_store_kv_fp4(
         _ptr(key_bits), key_bits.shape[1], _ptr(value_bits), value_bits.shape[1],
-        _ptr(kv_cache), _ptr(kv_cache, side_bytes), _ptr(slot_mapping), T,
+        SRC_DTYPES[dtype], _ptr(kv_cache), _ptr(kv_cache, side_bytes), _ptr(slot_mapping), T,
         num_heads, head_size, block_size, kv_cache.shape[0], page_stride, layout,
         float(k_scale), float(v_scale))

@@ -37,7 +37,7 @@
  *     codes E2M1(x * (gs/sf)), element 2m in the low nibble of byte m.
  *   - Out-of-range indices (page ids, block-table columns, output rows,
  *     slots past the cache) are skipped, never dereferenced.
- *   - Inputs are finite bf16; non-finite inputs are outside the contract
+ *   - Inputs are finite bf16 or fp16; non-finite inputs are outside the contract
  *     (the oracle still returns deterministic bytes for them).
  */
 #include <math.h>
@@ -54,6 +54,33 @@ float oracle_bf16_to_f32(uint16_t h)
     float f;
     memcpy(&f, &bits, sizeof f);
     return f;
+}
+
+/* binary16 -> binary32, from the format's definition: sign, 5-bit exponent
+ * (bias 15), 10-bit fraction; exponent 0 is subnormal (m * 2^-24), 31 is
+ * infinity / NaN.  Every value is exact in binary32. */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp(1024.0 + m, e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* Source element widening.  The NVFP4 store's dispatcher on the vLLM page
+ * instantiates the kernel for both 16-bit float types (fp16 and bf16). */
+#define ORACLE_SRC_BF16 0
+#define ORACLE_SRC_F16 1
+static float widen(uint16_t h, int32_t src_dtype)
+{
+    return src_dtype == ORACLE_SRC_F16 ? oracle_f16_to_f32(h) : oracle_bf16_to_f32(h);
 }
 
 /* ------------------------------------------------------------------ */
@@ -216,12 +243,13 @@ void oracle_gather_indexer_k_fp8(const uint8_t *kv_cache, uint8_t *k_fp8,
 /* ------------------------------------------------------------------ */
 /* fp8 per-token quantize and scatter into the indexer page.             */
 /* For token t with slot >= 0: page = slot / B, off = slot % B;          */
-/*   x_i = bf16 k[t, i];  amax = max |x_i|;  s = amax / 448 (binary32);   */
+/*   x_i = k[t, i] (bf16 or fp16, widened exactly);                       */
+/*   amax = max |x_i|;  s = amax / 448 (binary32);                        */
 /*   code_i = E4M3(x_i / s)  (x_i itself when s == 0);                   */
 /*   page codes [off*D .. +D) = code, page scale bytes [B*D + off*4 .. +4) */
 /*   = s, little-endian.  Slots < 0, and pages past the cache, skip.     */
 /* ------------------------------------------------------------------ */
-void oracle_store_indexer_k_fp8(const uint16_t *k, int64_t k_row_stride,
+void oracle_store_indexer_k_fp8(const uint16_t *k, int64_t k_row_stride, int32_t src_dtype,
                                 const int64_t *slot_mapping, int64_t num_tokens,
                                 uint8_t *kv_cache, int64_t num_blocks,
                                 int64_t cache_block_stride, int32_t block_size,
@@ -242,14 +270,14 @@ void oracle_store_indexer_k_fp8(const uint16_t *k, int64_t k_row_stride,
         if (page >= num_blocks)
             continue;
         for (i = 0; i < head_dim; ++i) {
-            float a = fabsf(oracle_bf16_to_f32(src[i]));
+            float a = fabsf(widen(src[i], src_dtype));
             if (a > amax)
                 amax = a;
         }
         s = amax / 448.0f;
         base = kv_cache + page * cache_block_stride;
         for (i = 0; i < head_dim; ++i) {
-            float x = oracle_bf16_to_f32(src[i]);
+            float x = widen(src[i], src_dtype);
             float y = (s == 0.0f) ? x : x / s;
             base[off * head_dim + i] = oracle_e4m3_encode(y);
         }
@@ -281,7 +309,7 @@ void oracle_store_indexer_k_fp8(const uint16_t *k, int64_t k_row_stride,
 /*   scale byte sf8 at (off, g) for K and at the swizzled position for V. */
 /* ------------------------------------------------------------------ */
 void oracle_store_kv_fp4(const uint16_t *key, int64_t key_row_stride,
-                         const uint16_t *value, int64_t value_row_stride,
+                         const uint16_t *value, int64_t value_row_stride, int32_t src_dtype,
                          uint8_t *key_cache, uint8_t *value_cache,
                          const int64_t *slot_mapping, int64_t num_tokens,
                          int32_t num_heads, int32_t head_size, int32_t block_size,
@@ -320,7 +348,7 @@ void oracle_store_kv_fp4(const uint16_t *key, int64_t key_row_stride,
                     int64_t data_off, scale_off, row, col;
                     for (k2 = 0; k2 < 16; ++k2) {
                         float a;
-                        x[k2] = oracle_bf16_to_f32(src[(int64_t)h * head_size + g * 16 + k2]);
+                        x[k2] = widen(src[(int64_t)h * head_size + g * 16 + k2], src_dtype);
                         a = fabsf(x[k2]);
                         if (a > amax)
                             amax = a;

@@ -61,6 +61,15 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def f16_bits(x: np.ndarray) -> np.ndarray:
+    """binary32 -> binary16 (RNE, numpy) as uint16 bit patterns."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def half_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f16_bits(x) if dtype == "f16" else bf16_bits(x)
+
+
 def random_bytes(g: np.random.Generator, shape) -> np.ndarray:
     return g.integers(0, 256, size=shape, dtype=np.uint8)
 
@@ -110,6 +119,7 @@ class IndexerWorkload:
     k_fp8_init: np.ndarray           # uint8 [T + guard, D] sentinel bytes
     k_scale_init: np.ndarray         # uint8 [T + guard, 4] sentinel bytes
     notes: dict = field(default_factory=dict)
+    dtype: str = "bf16"              # source element type of k_bits: "bf16" or "f16"
 
     @property
     def page_bytes(self) -> int:
@@ -122,7 +132,7 @@ class IndexerWorkload:
 
 def _indexer(name, seed, lens, block_size, head_dim, num_blocks, width=None,
              poison=False, outlier_frac=0.0, outlier_mult=20.0, guard=3,
-             drop_frac=0.0, k_override=None):
+             drop_frac=0.0, k_override=None, dtype="bf16"):
     g = rng(seed)
     lens = [int(x) for x in lens]
     poison_id = None
@@ -144,7 +154,7 @@ def _indexer(name, seed, lens, block_size, head_dim, num_blocks, width=None,
             n_out = int(round(outlier_frac * T))
             rows = g.choice(T, size=n_out, replace=False)
             kf[rows] *= np.float32(outlier_mult)
-    k_bits = bf16_bits(kf)
+    k_bits = half_bits(kf, dtype)
     slots = slots_from_table(table, lens, block_size)
     if drop_frac > 0:
         n_drop = int(np.floor(drop_frac * T))
@@ -155,7 +165,7 @@ def _indexer(name, seed, lens, block_size, head_dim, num_blocks, width=None,
     k_scale = random_bytes(g, (T + guard, INDEXER_SCALE_BYTES))
     return IndexerWorkload(name, block_size, head_dim, num_blocks, lens, cu, table,
                            k_bits, slots, cache, k_fp8, k_scale,
-                           notes={"poison_page": poison_id, "seed": seed})
+                           notes={"poison_page": poison_id, "seed": seed}, dtype=dtype)
 
 
 def c1_tiny_gather() -> IndexerWorkload:
@@ -177,21 +187,21 @@ def c3_long_ragged() -> IndexerWorkload:
                     poison=True)
 
 
-def c4_roundtrip() -> IndexerWorkload:
+def c4_roundtrip(dtype="bf16") -> IndexerWorkload:
     """16 requests x 512 tokens stored into a 256-page cache (5% of slots = -1),
     then gathered back."""
     return _indexer("roundtrip_16x512", 1003, [512] * 16, 64, 128, 256, width=8,
-                    drop_frac=0.05)
+                    drop_frac=0.05, dtype=dtype)
 
 
 def small_indexer(seed, lens, block_size=64, head_dim=128, num_blocks=None, width=None,
-                  drop_frac=0.0, poison=False):
+                  drop_frac=0.0, poison=False, dtype="bf16"):
     """Small random case for the property tests."""
     need = sum(-(-int(n) // block_size) for n in lens)
     if num_blocks is None:
         num_blocks = max(need + 2, 4)
     return _indexer(f"small_{seed}", seed, lens, block_size, head_dim, num_blocks,
-                    width=width, drop_frac=drop_frac, poison=poison)
+                    width=width, drop_frac=drop_frac, poison=poison, dtype=dtype)
 
 
 @dataclass
@@ -209,6 +219,7 @@ class Fp4Workload:
     k_scale: float
     v_scale: float
     cache_init: np.ndarray           # uint8 [num_blocks, 2, side_bytes]
+    dtype: str = "bf16"              # source element type: "bf16" or "f16"
 
     @property
     def side_bytes(self) -> int:
@@ -220,7 +231,7 @@ class Fp4Workload:
 
 
 def _fp4(name, seed, T, H, D, B, num_blocks, layout=0, slots=None, drop_frac=0.05,
-         lens=None):
+         lens=None, dtype="bf16"):
     g = rng(seed)
     if lens is not None:
         table, _ = _pages_table(g, lens, B, num_blocks)
@@ -238,20 +249,21 @@ def _fp4(name, seed, T, H, D, B, num_blocks, layout=0, slots=None, drop_frac=0.0
     k_scale, v_scale = (float(np.float32(v)) for v in g.uniform(0.5, 2.0, size=2))
     side = H * B * (D // 2 + D // 16)
     cache = random_bytes(g, (num_blocks, 2, side))
-    return Fp4Workload(name, H, D, B, num_blocks, layout, bf16_bits(kf), bf16_bits(vf),
-                       slot_mapping, k_scale, v_scale, cache)
+    return Fp4Workload(name, H, D, B, num_blocks, layout, half_bits(kf, dtype),
+                       half_bits(vf, dtype), slot_mapping, k_scale, v_scale, cache, dtype)
 
 
-def c5_nvfp4_store(layout=0) -> Fp4Workload:
+def c5_nvfp4_store(layout=0, dtype="bf16") -> Fp4Workload:
     """K and V [4096, 8, 128], B=16, 512 pages, 5% of slots = -1, scales in [0.5, 2]."""
-    return _fp4("nvfp4_4096x8x128", 1004, 4096, 8, 128, 16, 512, layout=layout)
+    return _fp4("nvfp4_4096x8x128", 1004, 4096, 8, 128, 16, 512, layout=layout, dtype=dtype)
 
 
-def small_fp4(seed, T, H=2, D=64, B=8, num_blocks=None, layout=0, drop_frac=0.1):
+def small_fp4(seed, T, H=2, D=64, B=8, num_blocks=None, layout=0, drop_frac=0.1,
+              dtype="bf16"):
     if num_blocks is None:
         num_blocks = max(-(-T // B) + 2, 2)
     return _fp4(f"small_fp4_{seed}", seed, T, H, D, B, num_blocks, layout=layout,
-                drop_frac=drop_frac)
+                drop_frac=drop_frac, dtype=dtype)
 
 
 def prefill_fp4(num_reqs=256, req_len=1000, H=8, D=128, B=16, seed=1005) -> Fp4Workload:
