@@ -4,7 +4,7 @@
  *
  * Three operations, named after the pages that define them:
  *
- *   pkv_store_indexer_k_fp8   quantize bf16 keys per token to OCP fp8 E4M3
+ *   pkv_store_indexer_k_fp8   quantize bf16/fp16 keys per token to OCP fp8 E4M3
  *                             with a binary32 scale (amax/448) and scatter
  *                             codes and scale into indexer K cache pages by
  *                             slot_mapping.
@@ -42,7 +42,7 @@
  *    block-table column >= max_blocks_per_req, an output row outside
  *    [0, num_tokens).  Duplicate slots, or overlapping cu_seq_lens ranges,
  *    give unspecified (but in-bounds) results.
- *  - Numerics are defined for finite bf16 inputs; non-finite inputs give
+ *  - Numerics are defined for finite bf16/fp16 inputs; non-finite inputs give
  *    unspecified codes (memory access is unaffected).
  *  - Results are bit-exact and independent of the launch configuration.
  */
@@ -64,8 +64,13 @@ extern "C" {
 #define PKV_LAYOUT_HND 0       /* per page side: data [H][B][D/2], scales [H][B][D/16] */
 #define PKV_LAYOUT_NHD 1       /* per page side: data [B][H][D/2], scales [B][H][D/16] */
 
+/* Source element types of the stores (the NVFP4 store's dispatcher on the
+ * vLLM page covers both 16-bit float types); both widen exactly to binary32. */
+#define PKV_DTYPE_BF16 0
+#define PKV_DTYPE_F16 1
+
 /* ABI version of this header; bumped when a signature changes. */
-#define PKV_ABI_VERSION 1
+#define PKV_ABI_VERSION 2
 int pkv_abi_version(void);
 
 /* Message for the last non-zero status on this thread ("" if none). */
@@ -110,20 +115,22 @@ int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_scale,
  *
  * For each token t with slot = slot_mapping[t] >= 0 and
  * page = slot / block_size < num_blocks, off = slot % block_size:
- *     x_i  = bf16 k[t*k_row_stride + i], i < head_dim
+ *     x_i  = k[t*k_row_stride + i], i < head_dim, widened exactly
  *     s    = binary32(max_i |x_i| / 448)              (IEEE division, RNE)
  *     code = E4M3(binary32(x_i / s))   (x_i itself when s == 0; OCP E4M3FN,
  *                                       round to nearest even, saturating)
  *     page bytes [off*head_dim + i]            = code_i
  *     page bytes [block_size*head_dim + off*4, +4) = s, little-endian
  *
- *   k             bf16 [num_tokens, >= head_dim] with row stride k_row_stride
- *                 ELEMENTS (>= head_dim, multiple of 8); 16-byte aligned.
+ *   k             bf16 or fp16 (k_dtype) [num_tokens, >= head_dim] with row
+ *                 stride k_row_stride ELEMENTS (>= head_dim, multiple of 8);
+ *                 16-byte aligned.
+ *   k_dtype       PKV_DTYPE_BF16 or PKV_DTYPE_F16.
  *   slot_mapping  int64 [num_tokens]; 8-byte aligned.
  *   kv_cache      written; 16-byte aligned; stride as for the gather.
  *   head_dim      multiple of 16, at most 1024.
  */
-int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride,
+int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride, int32_t k_dtype,
                             const int64_t *slot_mapping, int64_t num_tokens,
                             void *kv_cache, int64_t num_blocks,
                             int64_t cache_block_stride, int32_t block_size,
@@ -147,9 +154,11 @@ int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride,
  *     scale byte sf8 at (row off, column g) for K; for V at the swizzled
  *     (row (off/4)*4 + g/(S/4), column (g % (S/4))*4 + off%4).
  *
- *   key, value      bf16 [num_tokens, num_heads, head_size]; heads and
- *                   elements contiguous, token stride *_row_stride ELEMENTS
- *                   (>= H*D, multiple of 8); 16-byte aligned.
+ *   key, value      bf16 or fp16 (src_dtype) [num_tokens, num_heads,
+ *                   head_size]; heads and elements contiguous, token stride
+ *                   *_row_stride ELEMENTS (>= H*D, multiple of 8); 16-byte
+ *                   aligned.
+ *   src_dtype       PKV_DTYPE_BF16 or PKV_DTYPE_F16.
  *   key_cache,
  *   value_cache     written; 8-byte aligned; page_stride multiple of 8 and
  *                   >= the side size H*B*(D/2 + D/16).
@@ -160,7 +169,8 @@ int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride,
  *   block_size      multiple of 4.
  */
 int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
-                     int64_t value_row_stride, void *key_cache, void *value_cache,
+                     int64_t value_row_stride, int32_t src_dtype, void *key_cache,
+                     void *value_cache,
                      const int64_t *slot_mapping, int64_t num_tokens,
                      int32_t num_heads, int32_t head_size, int32_t block_size,
                      int64_t num_blocks, int64_t page_stride, int32_t layout,

@@ -24,6 +24,8 @@ __all__ = [
 
 LAYOUT_HND = 0
 LAYOUT_NHD = 1
+DTYPE_BF16 = 0
+DTYPE_F16 = 1
 SCALE_BYTES = 4
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
@@ -66,9 +68,9 @@ def _load():
     lib.pkv_abi_version.restype = ctypes.c_int
     lib.pkv_last_error.restype = ctypes.c_char_p
     lib.pkv_gather_indexer_k_fp8.argtypes = [P, P, P, P, P, i32, i32, i64, i64, i64, i32, i32, P]
-    lib.pkv_store_indexer_k_fp8.argtypes = [P, i64, P, i64, P, i64, i64, i32, i32, P]
-    lib.pkv_store_kv_fp4.argtypes = [P, i64, P, i64, P, P, P, i64, i32, i32, i32, i64, i64, i32,
-                                     P, P, P]
+    lib.pkv_store_indexer_k_fp8.argtypes = [P, i64, i32, P, i64, P, i64, i64, i32, i32, P]
+    lib.pkv_store_kv_fp4.argtypes = [P, i64, P, i64, i32, P, P, P, i64, i32, i32, i32, i64, i64,
+                                     i32, P, P, P]
     lib.pkv_diag_encode_e4m3.argtypes = [P, P, i64, P]
     lib.pkv_diag_encode_e2m1.argtypes = [P, P, i64, P]
     for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
@@ -105,6 +107,14 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     return t
+
+
+def _src_dtype(t: torch.Tensor, name: str) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float16:
+        return DTYPE_F16
+    raise TypeError(f"{name} must be bfloat16 or float16, got {t.dtype}")
 
 
 def _contig(t: torch.Tensor, name: str):
@@ -164,8 +174,9 @@ def pkv_gather_indexer_k_fp8(kv_cache, k_fp8, k_scale, block_table, cu_seq_lens,
 
 def pkv_store_indexer_k_fp8(k, slot_mapping, kv_cache, block_size: int | None = None,
                             stream=None):
-    """fp8 per-token quantize of bf16 k [num_tokens, D] and scatter into kv_cache."""
-    _dev(k, "k", torch.bfloat16)
+    """fp8 per-token quantize of bf16/fp16 k [num_tokens, D] and scatter into kv_cache."""
+    _dev(k, "k")
+    k_dtype = _src_dtype(k, "k")
     _dev(slot_mapping, "slot_mapping", torch.int64)
     _dev(kv_cache, "kv_cache", torch.uint8)
     _contig(slot_mapping, "slot_mapping")
@@ -181,13 +192,13 @@ def pkv_store_indexer_k_fp8(k, slot_mapping, kv_cache, block_size: int | None = 
     if kv_cache.stride(-1) != 1:
         raise ValueError("kv_cache pages must be contiguous")
     _check(_lib.pkv_store_indexer_k_fp8(
-        k.data_ptr(), k.stride(0), slot_mapping.data_ptr(), num_tokens, kv_cache.data_ptr(),
+        k.data_ptr(), k.stride(0), k_dtype, slot_mapping.data_ptr(), num_tokens, kv_cache.data_ptr(),
         kv_cache.shape[0], kv_cache.stride(0), block_size, head_dim, _stream(stream)))
 
 
 def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, v_scale,
                      block_size: int | None = None, layout: int | None = None, stream=None):
-    """NVFP4 store of bf16 key/value [num_tokens, H, D] into kv_cache[:,0] / kv_cache[:,1].
+    """NVFP4 store of bf16/fp16 key/value [num_tokens, H, D] into kv_cache[:,0] / kv_cache[:,1].
 
     key_cache / value_cache: uint8 views of the two page sides.  A 4-D
     [num_blocks, block_size, num_heads, D/2 + D/16] view supplies block_size
@@ -195,8 +206,11 @@ def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, 
     page's dispatcher does; a 2-D [num_blocks, side_bytes] view needs both
     passed explicitly.  k_scale / v_scale: float32 device scalars.
     """
-    _dev(key, "key", torch.bfloat16)
-    _dev(value, "value", torch.bfloat16)
+    _dev(key, "key")
+    _dev(value, "value")
+    src_dtype = _src_dtype(key, "key")
+    if value.dtype != key.dtype:
+        raise TypeError("key and value must have the same dtype")
     _dev(key_cache, "key_cache", torch.uint8)
     _dev(value_cache, "value_cache", torch.uint8)
     _dev(slot_mapping, "slot_mapping", torch.int64)
@@ -226,7 +240,8 @@ def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, 
     if key_cache.stride(0) != value_cache.stride(0) or key_cache.shape[0] != value_cache.shape[0]:
         raise ValueError("key_cache and value_cache must share num_blocks and page stride")
     _check(_lib.pkv_store_kv_fp4(
-        key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0), key_cache.data_ptr(),
+        key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0), src_dtype,
+        key_cache.data_ptr(),
         value_cache.data_ptr(), slot_mapping.data_ptr(), num_tokens, num_heads, head_size,
         block_size, key_cache.shape[0], key_cache.stride(0), layout, k_scale.data_ptr(),
         v_scale.data_ptr(), _stream(stream)))

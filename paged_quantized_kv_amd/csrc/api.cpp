@@ -98,14 +98,17 @@ int pkv_gather_indexer_k_fp8(const void* kv_cache, void* k_fp8, void* k_scale,
   return launched(pkv::launch_gather_indexer_k_fp8(a, static_cast<hipStream_t>(stream)), op);
 }
 
-int pkv_store_indexer_k_fp8(const void* k, int64_t k_row_stride, const int64_t* slot_mapping,
-                            int64_t num_tokens, void* kv_cache, int64_t num_blocks,
+int pkv_store_indexer_k_fp8(const void* k, int64_t k_row_stride, int32_t k_dtype,
+                            const int64_t* slot_mapping, int64_t num_tokens, void* kv_cache,
+                            int64_t num_blocks,
                             int64_t cache_block_stride, int32_t block_size, int32_t head_dim,
                             void* stream) {
   static const char* op = "pkv_store_indexer_k_fp8";
   if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens must be >= 0, got %lld", op, (long long)num_tokens);
   if (int rc = check_indexer_geometry(op, num_blocks, cache_block_stride, block_size, head_dim)) return rc;
   if (head_dim > 1024) return fail(PKV_EUNSUPPORTED, "%s: head_dim must be <= 1024, got %d", op, head_dim);
+  if (k_dtype != PKV_DTYPE_BF16 && k_dtype != PKV_DTYPE_F16)
+    return fail(PKV_EINVAL, "%s: k_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, k_dtype);
   if (k_row_stride < head_dim)
     return fail(PKV_EINVAL, "%s: k_row_stride %lld < head_dim %d", op, (long long)k_row_stride, head_dim);
   if (k_row_stride % 8 != 0)
@@ -116,14 +119,15 @@ int pkv_store_indexer_k_fp8(const void* k, int64_t k_row_stride, const int64_t* 
     return fail(PKV_EALIGN, "%s: k and kv_cache must be 16-byte aligned", op);
   if (!aligned(slot_mapping, 8)) return fail(PKV_EALIGN, "%s: slot_mapping must be 8-byte aligned", op);
   if (num_tokens > ((int64_t)1 << 40)) return fail(PKV_EUNSUPPORTED, "%s: num_tokens too large", op);
-  pkv::StoreFp8Args a{static_cast<const uint16_t*>(k), k_row_stride, slot_mapping, num_tokens,
+  pkv::StoreFp8Args a{static_cast<const uint16_t*>(k), k_row_stride, k_dtype, slot_mapping, num_tokens,
                       static_cast<uint8_t*>(kv_cache), num_blocks, cache_block_stride, block_size,
                       log2_or_neg(block_size), head_dim};
   return launched(pkv::launch_store_indexer_k_fp8(a, static_cast<hipStream_t>(stream)), op);
 }
 
 int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,
-                     int64_t value_row_stride, void* key_cache, void* value_cache,
+                     int64_t value_row_stride, int32_t src_dtype, void* key_cache,
+                     void* value_cache,
                      const int64_t* slot_mapping, int64_t num_tokens, int32_t num_heads,
                      int32_t head_size, int32_t block_size, int64_t num_blocks, int64_t page_stride,
                      int32_t layout, const float* k_scale, const float* v_scale, void* stream) {
@@ -141,6 +145,8 @@ int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,
     return fail(PKV_EUNSUPPORTED, "%s: head_size must be a multiple of 64 for the V-scale swizzle, got %d", op, head_size);
   if (block_size % 4 != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size must be divisible by 4 for the NVFP4 swizzle, got %d", op, block_size);
+  if (src_dtype != PKV_DTYPE_BF16 && src_dtype != PKV_DTYPE_F16)
+    return fail(PKV_EINVAL, "%s: src_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, src_dtype);
   if (layout != PKV_LAYOUT_HND && layout != PKV_LAYOUT_NHD)
     return fail(PKV_EINVAL, "%s: layout must be PKV_LAYOUT_HND or PKV_LAYOUT_NHD, got %d", op, layout);
   const int64_t hd = (int64_t)num_heads * head_size;
@@ -164,7 +170,7 @@ int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,
   if (!aligned(k_scale, 4) || !aligned(v_scale, 4))
     return fail(PKV_EALIGN, "%s: k_scale and v_scale must be 4-byte aligned", op);
   pkv::StoreFp4Args a{static_cast<const uint16_t*>(key), key_row_stride,
-                      static_cast<const uint16_t*>(value), value_row_stride,
+                      static_cast<const uint16_t*>(value), value_row_stride, src_dtype,
                       static_cast<uint8_t*>(key_cache), static_cast<uint8_t*>(value_cache),
                       slot_mapping, num_tokens, num_heads, head_size, block_size,
                       log2_or_neg(block_size), num_blocks, page_stride, layout, k_scale, v_scale};

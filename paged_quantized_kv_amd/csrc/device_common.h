@@ -25,6 +25,26 @@ __device__ __forceinline__ void unpack8(const u32x4 v, float* x) {
   x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
 }
 
+// 8 fp16 packed in a u32x4 -> 8 floats (exact, subnormals included).
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+__device__ __forceinline__ void unpack8_f16(const u32x4 v, float* x) {
+  x[0] = f16_lo(v.x); x[1] = f16_hi(v.x);
+  x[2] = f16_lo(v.y); x[3] = f16_hi(v.y);
+  x[4] = f16_lo(v.z); x[5] = f16_hi(v.z);
+  x[6] = f16_lo(v.w); x[7] = f16_hi(v.w);
+}
+
+// Widen 8 16-bit source elements: fp16 when kF16, else bf16.
+template <bool kF16>
+__device__ __forceinline__ void unpack8_src(const u32x4 v, float* x) {
+  if constexpr (kF16) unpack8_f16(v, x); else unpack8(v, x);
+}
+
 // |x| as a binary32 bit pattern; for non-negative floats the unsigned
 // integer order is the numeric order, so max-reductions run on integers.
 __device__ __forceinline__ uint32_t abs_bits(float x) { return __float_as_uint(x) & 0x7fffffffu; }

@@ -37,6 +37,7 @@ struct GatherArgs {
 struct StoreFp8Args {
   const uint16_t* k;
   int64_t k_row_stride;
+  int32_t k_dtype;  // PKV_DTYPE_BF16 / PKV_DTYPE_F16
   const int64_t* slot_mapping;
   int64_t num_tokens;
   uint8_t* kv_cache;
@@ -52,6 +53,7 @@ struct StoreFp4Args {
   int64_t key_row_stride;
   const uint16_t* value;
   int64_t value_row_stride;
+  int32_t src_dtype;  // PKV_DTYPE_BF16 / PKV_DTYPE_F16
   uint8_t* key_cache;
   uint8_t* value_cache;
   const int64_t* slot_mapping;

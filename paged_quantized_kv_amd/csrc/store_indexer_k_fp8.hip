@@ -3,6 +3,7 @@
 // gather_indexer_k_quant_cache kernel" reads.  For every token with a
 // non-negative slot: s = amax/448 in binary32, codes E4M3(x/s) (OCP E4M3FN,
 // round to nearest even), 4 scale bytes after the page's code region.
+// Source elements are bf16 or fp16, widened exactly.
 //
 // Mapping: kLanes lanes per token, 8 bf16 elements (one 16-byte load) per
 // lane and chunk, so the lanes of a token read its row with contiguous
@@ -21,6 +22,7 @@
 // here |y| <= 448 * (1 + 2^-8) even for subnormal scales.
 #include "device_common.h"
 #include "launch.h"
+#include "pkv.h"
 
 namespace pkv {
 
@@ -36,7 +38,7 @@ constexpr int kStoreUnroll = PKV_STORE8_UNROLL;  // token groups per wave in fli
 // kLanes lanes per token (a power of two), each holding kChunks runs of 8
 // elements: lane l of a token takes elements [8*(l + c*kLanes), +8), so the
 // lanes of a token read its row with contiguous 16-byte loads.
-template <int kLanes, int kChunks>
+template <int kLanes, int kChunks, bool kF16>
 __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
     const uint16_t* __restrict__ k, int64_t k_row_stride,
     const int64_t* __restrict__ slot_mapping, int64_t num_tokens, uint8_t* __restrict__ kv_cache,
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
     uint32_t m = 0;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      unpack8(xv[u][c], x[c]);
+      unpack8_src<kF16>(xv[u][c], x[c]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[c][i]));
     }
@@ -108,15 +110,21 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
   }
 }
 
-template <int kLanes, int kChunks>
-int launch_lanes(const StoreFp8Args& a, hipStream_t stream) {
+template <int kLanes, int kChunks, bool kF16>
+int launch_lanes_t(const StoreFp8Args& a, hipStream_t stream) {
   constexpr int64_t kTokensPerBlock = (kStoreThreads / kWave) * (kWave / kLanes) * kStoreUnroll;
   const int64_t blocks = (a.num_tokens + kTokensPerBlock - 1) / kTokensPerBlock;
-  hipLaunchKernelGGL((store_indexer_k_fp8_kernel<kLanes, kChunks>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((store_indexer_k_fp8_kernel<kLanes, kChunks, kF16>), dim3((unsigned)blocks),
                      dim3(kStoreThreads), 0, stream, a.k, a.k_row_stride, a.slot_mapping,
                      a.num_tokens, a.kv_cache, a.num_blocks, a.cache_block_stride, a.block_size,
                      a.log2_block_size, a.head_dim);
   return (int)hipGetLastError();
+}
+
+template <int kLanes, int kChunks>
+int launch_lanes(const StoreFp8Args& a, hipStream_t stream) {
+  return a.k_dtype == PKV_DTYPE_F16 ? launch_lanes_t<kLanes, kChunks, true>(a, stream)
+                                    : launch_lanes_t<kLanes, kChunks, false>(a, stream);
 }
 
 }  // namespace

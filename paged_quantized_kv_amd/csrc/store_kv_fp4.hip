@@ -1,7 +1,8 @@
 // NVFP4 K/V store (vLLM source nvfp4_kv_cache_kernels.cu: header comment,
 // swizzle_scale_offset, reshape_and_cache_nvfp4_kernel,
 // reshape_and_cache_nvfp4_dispatch).  Each 16-element block of a token's K
-// or V head becomes 8 bytes of packed E2M1 codes plus one E4M3 block scale;
+// or V head (bf16 or fp16, as the page's dispatcher instantiates it) becomes
+// 8 bytes of packed E2M1 codes plus one E4M3 block scale;
 // page sides are [data | scales], K scales linear, V scales in the 4x4-tile
 // swizzled order.
 //
@@ -32,6 +33,7 @@
 // saturating E4M3 result for any sf >= 448.
 #include "device_common.h"
 #include "launch.h"
+#include "pkv.h"
 
 namespace pkv {
 
@@ -65,6 +67,7 @@ __device__ __forceinline__ uint32_t from_lane_above(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + k, 0xF, 0xF, true);
 }
 
+template <bool kF16>
 __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
     const uint16_t* __restrict__ key, int64_t key_row_stride, const uint16_t* __restrict__ value,
     int64_t value_row_stride, uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
 #pragma unroll
     for (int k = 0; k < kFp4Unroll; ++k) {
       float x[8];
-      unpack8(xv[k], x);
+      unpack8_src<kF16>(xv[k], x);
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[i]));
@@ -210,7 +213,8 @@ int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream) {
     int64_t blocks = ((int64_t)items + kFp4Unroll * kFp4Threads - 1) / (kFp4Unroll * kFp4Threads);
     if (blocks > kFp4MaxBlocks) blocks = kFp4MaxBlocks;
     blocks = (blocks + kNumXcd - 1) / kNumXcd * kNumXcd;  // whole XCD ranges
-    hipLaunchKernelGGL(store_kv_fp4_kernel, dim3((unsigned)blocks), dim3(kFp4Threads), 0, stream,
+    auto kernel = a.src_dtype == PKV_DTYPE_F16 ? store_kv_fp4_kernel<true> : store_kv_fp4_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFp4Threads), 0, stream,
                        a.key, a.key_row_stride, a.value, a.value_row_stride, a.key_cache,
                        a.value_cache, a.slot_mapping, t0, items, a.num_heads, a.head_size,
                        a.block_size, a.log2_block_size, a.num_blocks, a.page_stride, a.layout,

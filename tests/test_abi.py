@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
     for s in declared_symbols():
         assert s in exported, s
         assert getattr(lib, s) is not None
-    assert pkv.abi_version() == 1
+    assert pkv.abi_version() == 2
 
 
 def lib():
@@ -84,10 +84,10 @@ def test_gather_empty_work_is_ok_without_launch(kw):
 
 
 def store8(**kw):
-    a = dict(k=A, ks=128, slots=A, T=10, cache=A, nb=4, stride=64 * 132, B=64, D=128)
+    a = dict(k=A, ks=128, dt=0, slots=A, T=10, cache=A, nb=4, stride=64 * 132, B=64, D=128)
     a.update(kw)
-    return lib().pkv_store_indexer_k_fp8(a["k"], a["ks"], a["slots"], a["T"], a["cache"],
-                                         a["nb"], a["stride"], a["B"], a["D"], None)
+    return lib().pkv_store_indexer_k_fp8(a["k"], a["ks"], a["dt"], a["slots"], a["T"],
+                                         a["cache"], a["nb"], a["stride"], a["B"], a["D"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -99,6 +99,8 @@ def store8(**kw):
     (dict(slots=A + 4), PKV_EALIGN),
     (dict(cache=0), PKV_EINVAL),
     (dict(T=-1), PKV_EINVAL),
+    (dict(dt=2), PKV_EINVAL),
+    (dict(dt=-1), PKV_EINVAL),
 ])
 def test_store_fp8_validation(kw, code):
     assert store8(**kw) == code
@@ -109,12 +111,12 @@ def test_store_fp8_empty_is_ok():
 
 
 def store4(**kw):
-    a = dict(key=A, kst=1024, val=A, vst=1024, kc=A, vc=A + 9216, slots=A, T=8, H=8, D=128,
-             B=16, nb=4, page=18432, layout=0, kscale=A, vscale=A)
+    a = dict(key=A, kst=1024, val=A, vst=1024, dt=0, kc=A, vc=A + 9216, slots=A, T=8, H=8,
+             D=128, B=16, nb=4, page=18432, layout=0, kscale=A, vscale=A)
     a.update(kw)
-    return lib().pkv_store_kv_fp4(a["key"], a["kst"], a["val"], a["vst"], a["kc"], a["vc"],
-                                  a["slots"], a["T"], a["H"], a["D"], a["B"], a["nb"], a["page"],
-                                  a["layout"], a["kscale"], a["vscale"], None)
+    return lib().pkv_store_kv_fp4(a["key"], a["kst"], a["val"], a["vst"], a["dt"], a["kc"],
+                                  a["vc"], a["slots"], a["T"], a["H"], a["D"], a["B"], a["nb"],
+                                  a["page"], a["layout"], a["kscale"], a["vscale"], None)
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -129,6 +131,7 @@ def store4(**kw):
     (dict(kscale=0), PKV_EINVAL, "null"),
     (dict(vc=A + 4), PKV_EALIGN, "8-byte"),
     (dict(H=0), PKV_EINVAL, "num_heads"),
+    (dict(dt=3), PKV_EINVAL, "src_dtype"),
 ])
 def test_store_fp4_validation(kw, code, msg):
     assert store4(**kw) == code

@@ -9,7 +9,9 @@ range, so checking every significand pair covers every exponent the kernels
 let through.  Two uses are checked here, each over its whole domain:
   * the fp8 store: x a bf16 value (128 significands), s = RN(amax/448) for
     any binary32 significand (2^23), i.e. 2^30 pairs;
-  * the NVFP4 block scale: t/6 for every binary32 significand t (2^23).
+  * the NVFP4 block scale: t/6 for every binary32 significand t (2^23);
+  * fp16 sources: every fp16 significand x (1024) against the scale of
+    every fp16 amax significand (1024).
 The program is plain C compiled with gcc (hardware fma when the host has
 it, glibc's correctly rounded fmaf otherwise)."""
 import os
@@ -48,7 +50,21 @@ int main(void) {
       if (b_of(markstein(x2, s, rs)) != b_of(x2 / s)) ++bad8;
     }
   }
-  printf("%ld %ld\n", bad6, bad8);
+  /* fp16 sources: x any fp16 significand (1024), s = RN(m/448) for every fp16
+     amax significand m (the only scales an fp16 token can produce) */
+  long bad16 = 0;
+  for (uint32_t ma = 0; ma < 1024; ++ma) {
+    float s = f_of(0x3F800000u | (ma << 13)) / 448.0f;
+    float rs = 1.0f / s;
+    for (uint32_t mx = 0; mx < 1024; ++mx) {
+      float x = f_of(0x3F800000u | (mx << 13));
+      for (int sh = 0; sh < 2; ++sh) {
+        float xx = sh ? x * 2.0f : x;
+        if (b_of(markstein(xx, s, rs)) != b_of(xx / s)) ++bad16;
+      }
+    }
+  }
+  printf("%ld %ld %ld\n", bad6, bad8, bad16);
   return 0;
 }
 """
@@ -64,6 +80,7 @@ def test_markstein_quotients_equal_ieee_division():
             flags.append("-mfma")
         subprocess.run(["gcc", *flags, c, "-o", exe, "-lm"], check=True)
         out = subprocess.run([exe], capture_output=True, text=True, check=True, timeout=600)
-    bad6, bad8 = map(int, out.stdout.split())
+    bad6, bad8, bad16 = map(int, out.stdout.split())
     assert bad6 == 0, f"{bad6} significands where the corrected t/6 differs"
     assert bad8 == 0, f"{bad8} significand pairs where the corrected x/s differs"
+    assert bad16 == 0, f"{bad16} fp16 significand pairs where the corrected x/s differs"

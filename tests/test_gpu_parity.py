@@ -28,8 +28,8 @@ def dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def bf16_dev(bits, shape=None):
-    t = dev(bits.view(np.int16)).view(torch.bfloat16)
+def bf16_dev(bits, shape=None, dtype="bf16"):
+    t = dev(bits.view(np.int16)).view(torch.float16 if dtype == "f16" else torch.bfloat16)
     return t if shape is None else t.view(*shape)
 
 
@@ -127,9 +127,10 @@ def run_store8(w, k_bits=None, slots=None, cache_np=None, row_pad=0):
     ref = c0.copy()
     if row_pad:
         kb = np.concatenate([kb, np.full((kb.shape[0], row_pad), 0x7F80, np.uint16)], axis=1)
-    oracle.store_indexer_k_fp8(np.ascontiguousarray(kb), sl, ref, w.block_size, w.head_dim)
+    oracle.store_indexer_k_fp8(np.ascontiguousarray(kb), sl, ref, w.block_size, w.head_dim,
+                               dtype=w.dtype)
     cache = dev(c0)
-    k = bf16_dev(np.ascontiguousarray(kb))[:, :w.head_dim]
+    k = bf16_dev(np.ascontiguousarray(kb), dtype=w.dtype)[:, :w.head_dim]
     pkv.pkv_store_indexer_k_fp8(k, dev(sl), cache, block_size=w.block_size)
     got = host(cache)
     np.testing.assert_array_equal(got, ref)
@@ -240,11 +241,12 @@ def run_store4(f, slots=None, layout=None, key_bits=None):
     kb = f.key_bits if key_bits is None else key_bits
     ref = f.cache_init.copy()
     oracle.store_kv_fp4(kb, f.value_bits, ref, sl, f.num_heads, f.head_size, f.block_size,
-                        layout, f.k_scale, f.v_scale)
+                        layout, f.k_scale, f.v_scale, dtype=f.dtype)
     c = dev(f.cache_init)
     T = sl.shape[0]
     shape = (T, f.num_heads, f.head_size)
-    pkv.pkv_store_kv_fp4(bf16_dev(kb, shape), bf16_dev(f.value_bits, shape), c[:, 0], c[:, 1],
+    pkv.pkv_store_kv_fp4(bf16_dev(kb, shape, f.dtype), bf16_dev(f.value_bits, shape, f.dtype),
+                         c[:, 0], c[:, 1],
                          dev(sl), torch.tensor([f.k_scale], dtype=torch.float32, device=DEV),
                          torch.tensor([f.v_scale], dtype=torch.float32, device=DEV),
                          block_size=f.block_size, layout=layout)
@@ -411,3 +413,60 @@ def test_store_fp4_global_scale_outside_table_range(scale):
     y = g.standard_normal((T, H, D)).astype(np.float32)
     f = _fp4_custom(x, y, B, scale, 1.0)
     run_store4(f)
+
+
+# ---------------------------------------------------------------- fp16 sources
+def test_store_fp8_f16_roundtrip_and_shapes():
+    banner("store fp8 f16 sources")
+    w = workloads.c4_roundtrip(dtype="f16")
+    run_store8(w)
+    for lens, bs, hd in (([37, 64, 1], 64, 16), ([65, 70], 32, 64), ([200], 64, 256),
+                         ([20], 8, 1024), ([90, 33], 48, 128)):
+        run_store8(workloads.small_indexer(sum(lens) + hd + 7, lens, block_size=bs,
+                                           head_dim=hd, drop_frac=0.1, dtype="f16"))
+
+
+def test_store_fp8_f16_value_edge_cases():
+    banner("store fp8 f16 value edge cases")
+    g = workloads.rng(321)
+    T, D = 256, 128
+    x = g.standard_normal((T, D)).astype(np.float32)
+    x[0] = 0.0
+    x[1, ::2] = -0.0
+    x[2] = np.float32(2.0 ** -24)                  # smallest fp16 subnormal
+    x[2, ::3] *= -1
+    x[3] *= np.float32(2.0 ** -16)                 # fp16 subnormal values
+    x[4] = np.float32(65504.0)                     # fp16 maximum
+    x[4, 1::2] = -1.0
+    x[5:64] *= np.exp2(g.integers(-20, 14, size=(59, 1))).astype(np.float32)
+    # every fp16 significand as amax
+    sig = ((np.arange(1024, dtype=np.uint32) << 13) | 0x3F800000).view(np.float32)
+    for i in range(64, 192):
+        row = sig[(i * 8) % 1024:(i * 8) % 1024 + D] if (i * 8) % 1024 + D <= 1024 else sig[:D]
+        x[i] = row * np.float32(2.0 ** -(i % 9))
+        x[i, 0] = sig[(i * 37) % 1024] * np.float32(4.0)
+    x = np.clip(x, -65504, 65504)
+    w = workloads.small_indexer(3, [T], drop_frac=0.0, dtype="f16")
+    run_store8(w, k_bits=workloads.f16_bits(x))
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+def test_store_fp4_c5_f16(layout):
+    f = workloads.c5_nvfp4_store(layout, dtype="f16")
+    banner(f"nvfp4 {f.name} f16 layout={layout}")
+    run_store4(f)
+
+
+def test_store_fp4_f16_shapes_and_edges():
+    banner("nvfp4 f16 shapes and edges")
+    for T, H, D, B, layout in ((37, 1, 64, 4, 0), (64, 3, 192, 12, 1), (33, 7, 128, 20, 0)):
+        run_store4(workloads.small_fp4(T * 17 + H, T, H=H, D=D, B=B, layout=layout,
+                                       dtype="f16"))
+    f = workloads.small_fp4(77, 48, H=2, D=128, B=16, drop_frac=0.0, dtype="f16")
+    x = f.key_bits.view(np.float16).astype(np.float32).reshape(48, 2, 8, 16).copy()
+    x[0] = 0.0
+    x[1] = np.float32(2.0 ** -24)
+    x[2] *= np.float32(2.0 ** -14)
+    x[3] = np.float32(65504.0)
+    x[3, :, :, 1::2] = -3.0
+    run_store4(f, key_bits=workloads.f16_bits(x.reshape(48, -1)))

@@ -29,10 +29,14 @@ def test_e4m3_decode_table_closed_form():
     assert np.isnan(oracle.e4m3_decode(np.array([0x7F, 0xFF], np.uint8))).all()
 
 
-def brute_nearest(a, grid):
+def brute_nearest(a, grid, chunk=8192):
     """Index of the nearest grid value; ties go to the even index; above the top
-    value saturates."""
-    a = np.asarray(a, np.float64)[:, None]
+    value saturates.  Every grid value is compared (in row chunks)."""
+    a = np.asarray(a, np.float64)
+    if a.size > chunk:
+        return np.concatenate([brute_nearest(a[i:i + chunk], grid, chunk)
+                               for i in range(0, a.size, chunk)])
+    a = a[:, None]
     d = np.abs(a - grid[None, :])
     best = d.min(axis=1, keepdims=True)
     cand = d == best
