@@ -116,6 +116,23 @@ __device__ __forceinline__ uint32_t group_max(uint32_t v) {
   return v;
 }
 
+// Orders the LDS accesses of one wave: what any lane wrote before the call
+// is visible to every lane of the same wave after it (LDS operations of one
+// wave execute in order; the fences keep the compiler from moving accesses
+// across the call).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Value of a 64-bit variable held by lane `src` (all lanes must take part).
+__device__ __forceinline__ int64_t lane_value(int64_t v, int src) {
+  const int lo = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)v);
+  const int hi = __builtin_amdgcn_ds_bpermute(src << 2, (int)(uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 // Inclusive prefix sum across the 64 lanes of a wave.
 __device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
   const int lane = threadIdx.x & (kWave - 1);

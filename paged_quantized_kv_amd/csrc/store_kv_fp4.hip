@@ -6,16 +6,32 @@
 // page sides are [data | scales], K scales linear, V scales in the 4x4-tile
 // swizzled order.
 //
-// Mapping: two lanes per 16-element block, 8 bf16 (one 16-byte load) per
-// lane.  Work items are half-blocks ordered (token, side, head, block,
-// half), so a wave-wide load reads 1 KB of one token side contiguously; the
-// block amax is a DPP swap between the two lanes, and each lane writes the
-// 4 code bytes of its half.  K scales, which are linear, leave as one dword
-// per 4 blocks (collected from neighbouring lanes with DPP row shifts); V
-// scales are single bytes at their swizzled positions.  Each lane issues the
-// loads of several items before it quantizes any of them, and the grid is
-// numbered so that each XCD takes one contiguous range of tokens: the tokens
-// that share a page then write its lines through one L2.
+// Two kernels share the block quantizer below; both give the same bytes.
+//
+// Tile kernel (head_size 64, 128 or 256, 16-byte aligned page sides): one
+// wave quantizes one (16-token tile, side, head).  Lane loads are 16 bytes
+// and contiguous over the wave, two lanes per 16-element block.  The wave
+// assembles the tile's code bytes and scale bytes in LDS in page order, then
+// writes them out 16 bytes per lane for the codes and one dword per lane for
+// the scales.  Every lane computes the address of what it writes from the
+// slot of its own token, so any slot_mapping is handled; when the tile's
+// tokens sit in consecutive slots of one page (as a prefill fills pages),
+// a wave's code store covers tile * head_size/2 contiguous bytes and its
+// scale store tile * head_size/16 contiguous bytes, whole cache lines.  A
+// V-scale dword holds one block scale of 4 tokens of one swizzle tile, so it
+// is written as a dword only when those 4 tokens are the 4 consecutive slots
+// of a tile; otherwise byte by byte.
+//
+// Generic kernel (any head_size that is a multiple of 64): work items are
+// half-blocks ordered (token, side, head, block, half), so a wave-wide load
+// reads 1 KB of one token side contiguously; each lane writes the 4 code
+// bytes of its half, K scales leave as one dword per 4 blocks (collected
+// from neighbouring lanes with DPP row shifts) and V scales as single bytes
+// at their swizzled positions.
+//
+// In both, workgroups are renumbered so that each XCD takes one contiguous
+// range of tokens: the tokens that share a page then write its lines
+// through one L2.
 //
 // Arithmetic per block, all binary32 with round-to-nearest-even:
 //   amax = max|x|;  sf = (amax * gs) / 6;  sf8 = E4M3(min(sf, 448))
@@ -40,11 +56,27 @@ namespace pkv {
 namespace {
 
 constexpr int kFp4Threads = 256;
+constexpr int kFp4Waves = kFp4Threads / kWave;
 
 #ifndef PKV_FP4_UNROLL
 #define PKV_FP4_UNROLL 2
 #endif
-constexpr int kFp4Unroll = PKV_FP4_UNROLL;  // half-blocks per lane in flight
+constexpr int kFp4Unroll = PKV_FP4_UNROLL;  // half-blocks per lane in flight (generic kernel)
+
+constexpr int kFp4Tile = 16;  // tokens per wave item (tile kernel)
+
+#ifndef PKV_FP4_NT_STORE
+#define PKV_FP4_NT_STORE 1
+#endif
+#ifndef PKV_FP4_NT_SCALE
+#define PKV_FP4_NT_SCALE 0
+#endif
+#ifndef PKV_FP4_WPE
+#define PKV_FP4_WPE 0
+#endif
+#ifndef PKV_FP4_NT_LOAD
+#define PKV_FP4_NT_LOAD 1
+#endif
 
 struct Div {
   // n / d and n % d for a positive divisor that may or may not be a power of two
@@ -67,6 +99,248 @@ __device__ __forceinline__ uint32_t from_lane_above(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + k, 0xF, 0xF, true);
 }
 
+// Per-side global scales gs = 1/k_scale, 1/v_scale, and RN(gs / M) for
+// M = 1..15 in LDS.  Called by every thread of the workgroup (barrier).
+struct GlobalScales {
+  float gs_k, gs_v;
+  bool table_k, table_v;  // gs in [2^-100, 2^100]: the LDS quotients are exact
+  __device__ __forceinline__ float gs(int kv) const { return kv ? gs_v : gs_k; }
+  __device__ __forceinline__ bool table(int kv) const { return kv ? table_v : table_k; }
+};
+__device__ __forceinline__ GlobalScales load_global_scales(const float* k_scale,
+                                                           const float* v_scale,
+                                                           float (*gs_over_m)[16]) {
+  GlobalScales g;
+  g.gs_k = 1.0f / *k_scale;
+  g.gs_v = 1.0f / *v_scale;
+  if (threadIdx.x < 32) {
+    const int side = threadIdx.x >> 4, mm = threadIdx.x & 15;
+    gs_over_m[side][mm] = mm ? g.gs(side) / (float)mm : 0.0f;
+  }
+  __syncthreads();
+  g.table_k = g.gs_k >= 0x1p-100f && g.gs_k <= 0x1p100f;
+  g.table_v = g.gs_v >= 0x1p-100f && g.gs_v <= 0x1p100f;
+  return g;
+}
+
+// Quantizes the 8 elements this lane holds, one half of a 16-element block
+// whose other half is in lane l ^ 1.  Returns the 4 code bytes (element 2m in
+// the low nibble of byte m) and the block's E4M3 scale in sf8.  Every lane of
+// the wave must call it (the block amax is a DPP swap).
+__device__ __forceinline__ uint32_t nvfp4_half_block(const float (&x)[8], float gs, bool table,
+                                                     const float* gs_over_m, uint32_t& sf8) {
+  constexpr float kSixth = 1.0f / 6.0f;  // RN(1/6)
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[i]));
+  m = max(m, dpp<kQuadSwap1>(m));  // the other half of the block
+  const float amax = __uint_as_float(m);
+  const float t6 = amax * gs;
+  const float q6 = t6 * kSixth;
+  const float sf = __builtin_fmaf(__builtin_fmaf(-q6, 6.0f, t6), kSixth, q6);  // = t6 / 6
+  sf8 = e4m3_pack2<false>(fminf(sf, 448.0f), 0.0f, 0u) & 0xffu;
+  // decode(sf8) = M * 2^p: normal codes M = 8 + mantissa, p = exponent - 10;
+  // subnormal codes M = mantissa, p = -9
+  const uint32_t ex = sf8 >> 3;
+  const uint32_t mm = ex ? 8u + (sf8 & 7u) : (sf8 & 7u);
+  const int p = ex ? (int)ex - 10 : -9;
+  float r;
+  if (table)
+    r = sf8 ? __builtin_ldexpf(gs_over_m[mm], -p) : 0.0f;
+  else
+    r = sf8 ? gs / e4m3_decode(sf8) : 0.0f;
+  uint32_t packed = e2m1_pack2<0>(x[0] * r, x[1] * r, 0u);
+  packed = e2m1_pack2<1>(x[2] * r, x[3] * r, packed);
+  packed = e2m1_pack2<2>(x[4] * r, x[5] * r, packed);
+  packed = e2m1_pack2<3>(x[6] * r, x[7] * r, packed);
+  return packed;
+}
+
+__device__ __forceinline__ u32x4 load_src(const u32x4* p) {
+  if constexpr (PKV_FP4_NT_LOAD) return load_stream(p);
+  else return *p;
+}
+
+__device__ __forceinline__ void store_codes16(uint8_t* p, u32x4 v) {
+  if constexpr (PKV_FP4_NT_STORE) store_stream(reinterpret_cast<u32x4*>(p), v);
+  else *reinterpret_cast<u32x4*>(p) = v;
+}
+
+__device__ __forceinline__ void store_scale4(uint8_t* p, uint32_t v) {
+  if constexpr (PKV_FP4_NT_SCALE) __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
+  else *reinterpret_cast<uint32_t*>(p) = v;
+}
+
+// Byte offset of V scale (off, g) inside its page side's scale region:
+// 4x4-tile swizzle of the per-head [B, S] tile, (t', s') =
+// ((off/4)*4 + g/(S/4), (g % (S/4))*4 + off%4).
+__device__ __forceinline__ int64_t v_scale_offset(int64_t off, int32_t g, int32_t S, int32_t h,
+                                                  int32_t num_heads, int32_t block_size,
+                                                  int32_t layout) {
+  const int32_t q4 = S / 4;
+  const int64_t row = (off >> 2) * 4 + g / q4;
+  const int64_t col = (int64_t)(g % q4) * 4 + (off & 3);
+  return layout == PKV_LAYOUT_HND ? ((int64_t)h * block_size + row) * S + col
+                                  : (row * num_heads + h) * S + col;
+}
+
+// ------------------------------------------------------------------ tile kernel
+template <int kD, bool kF16>
+__global__ __launch_bounds__(kFp4Threads)
+#if PKV_FP4_WPE
+__attribute__((amdgpu_waves_per_eu(PKV_FP4_WPE)))
+#endif
+void store_kv_fp4_tile_kernel(
+    const uint16_t* __restrict__ key, int64_t key_row_stride, const uint16_t* __restrict__ value,
+    int64_t value_row_stride, uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
+    const int64_t* __restrict__ slot_mapping, int64_t num_tokens, int64_t num_items,
+    int64_t num_logical_blocks, int32_t num_heads, int32_t block_size, int32_t log2_bs,
+    int64_t num_blocks, int64_t page_stride, int32_t layout, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale) {
+  constexpr int kC = kD / 8;                       // 16-byte source chunks per token head
+  constexpr int kS = kD / 16;                      // blocks (scale bytes) per token head
+  constexpr int kTokPerLoad = kWave / kC;          // tokens one wave-wide load covers
+  constexpr int kLoads = kFp4Tile / kTokPerLoad;   // loads per lane per item
+  constexpr int kDataBytes = kFp4Tile * kD / 2;    // code bytes of one item
+  constexpr int kDataChunks = kDataBytes / 16;     // 16-byte code chunks of one item
+  constexpr int kChunksPerTok = kD / 32;           // 16-byte code chunks per token head
+  constexpr int kScaleWords = kFp4Tile * kS / 4;   // scale dwords of one item
+  static_assert(kC % 2 == 0 && kWave % kC == 0 && kFp4Tile % kTokPerLoad == 0, "tile shape");
+  static_assert(kDataChunks % kWave == 0 || kDataChunks < kWave, "code chunks per lane");
+  static_assert(kScaleWords <= kWave && kS % 4 == 0, "scale words per lane");
+
+  __shared__ float gs_over_m[2][16];
+  __shared__ __align__(16) uint32_t data_img[kFp4Waves][kDataBytes / 4];
+  __shared__ __align__(16) uint32_t scale_img[kFp4Waves][kScaleWords];
+  const GlobalScales G = load_global_scales(k_scale, v_scale, gs_over_m);
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  uint32_t* dimg = data_img[wave];
+  uint32_t* simg = scale_img[wave];
+  uint8_t* simg8 = reinterpret_cast<uint8_t*>(simg);
+  const int64_t data_per_side = (int64_t)num_heads * block_size * (kD / 2);
+  const int32_t sides_heads = 2 * num_heads;
+
+  for (int64_t lb = xcd_contiguous_block(); lb < num_logical_blocks; lb += gridDim.x) {
+    const int64_t item = lb * kFp4Waves + wave;  // (tile, side, head)
+    if (item >= num_items) continue;
+    const int64_t tile = item / sides_heads;
+    const int32_t sh = (int32_t)(item - tile * sides_heads);
+    const int kv = sh >= num_heads;
+    const int32_t h = kv ? sh - num_heads : sh;
+    const int64_t t0 = tile * kFp4Tile;
+    const uint16_t* src = kv ? value : key;
+    const int64_t row_stride = kv ? value_row_stride : key_row_stride;
+
+    // slot of token t0 + (lane % 16); tokens past the end have slot -1
+    const int64_t my_t = t0 + (lane & (kFp4Tile - 1));
+    const int64_t my_slot = my_t < num_tokens ? slot_mapping[my_t] : -1;
+
+    // ---- loads: lane holds chunk c of token tk for each of kLoads loads
+    const int c = lane % kC;
+    u32x4 xv[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int64_t t = t0 + k * kTokPerLoad + lane / kC;
+      xv[k] = u32x4{0u, 0u, 0u, 0u};
+      if (t < num_tokens)
+        xv[k] = load_src(reinterpret_cast<const u32x4*>(src + t * row_stride + (int64_t)h * kD) + c);
+    }
+
+    // ---- quantize into the LDS images (codes [tok][kD/2]; K scales
+    // [tok][kS]; V scales [tok/4][g][tok%4], i.e. the swizzled order)
+    const float gs = G.gs(kv);
+    const bool table = G.table(kv);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int tk = k * kTokPerLoad + lane / kC;
+      float x[8];
+      unpack8_src<kF16>(xv[k], x);
+      uint32_t sf8;
+      const uint32_t packed = nvfp4_half_block(x, gs, table, gs_over_m[kv], sf8);
+      dimg[tk * kC + c] = packed;  // byte offset tk*kD/2 + 4c
+      if ((c & 1) == 0) {
+        const int g = c >> 1;
+        const int pos = kv ? (tk >> 2) * 4 * kS + g * 4 + (tk & 3) : tk * kS + g;
+        simg8[pos] = (uint8_t)sf8;
+      }
+    }
+    wave_sync();
+
+    // ---- code bytes: 16 bytes per lane, address from the chunk's token slot
+#pragma unroll
+    for (int q0 = 0; q0 < kDataChunks; q0 += kWave) {
+      const int q = q0 + lane;
+      const int tok = (q < kDataChunks ? q : 0) / kChunksPerTok;
+      const int64_t slot = lane_value(my_slot, tok);
+      if (q < kDataChunks && slot >= 0) {
+        int64_t page, off;
+        split_slot(slot, block_size, log2_bs, page, off);
+        if (page < num_blocks) {
+          uint8_t* side = (kv ? value_cache : key_cache) + page * page_stride;
+          const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h * block_size + off
+                                                       : off * num_heads + h;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(dimg + 4 * q);
+          store_codes16(side + row * (kD / 2) + (q % kChunksPerTok) * 16, v);
+        }
+      }
+    }
+
+    // ---- scale bytes: one dword per lane
+    const int sw = lane < kScaleWords ? lane : 0;
+    const uint32_t word = simg[sw];
+    if (kv == 0) {
+      const int tok = (4 * sw) / kS;
+      const int64_t slot = lane_value(my_slot, tok);
+      if (lane < kScaleWords && slot >= 0) {
+        int64_t page, off;
+        split_slot(slot, block_size, log2_bs, page, off);
+        if (page < num_blocks) {
+          uint8_t* scales = key_cache + page * page_stride + data_per_side;
+          const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h * block_size + off
+                                                       : off * num_heads + h;
+          store_scale4(scales + row * kS + (4 * sw) % kS, word);
+        }
+      }
+    } else {
+      // dword sw = block g of the 4 tokens 4*quad .. 4*quad+3
+      const int quad = sw / kS, g = sw % kS;
+      int64_t s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] = lane_value(my_slot, 4 * quad + i);
+      if (lane < kScaleWords) {
+        const bool whole = s4[0] >= 0 && (s4[0] & 3) == 0 && s4[1] == s4[0] + 1 &&
+                           s4[2] == s4[0] + 2 && s4[3] == s4[0] + 3;
+        if (whole) {
+          // 4 consecutive slots starting at a multiple of 4: one page (block
+          // sizes are multiples of 4), one swizzle tile, one dword
+          int64_t page, off;
+          split_slot(s4[0], block_size, log2_bs, page, off);
+          if (page < num_blocks) {
+            uint8_t* scales = value_cache + page * page_stride + data_per_side;
+            store_scale4(scales + v_scale_offset(off, g, kS, h, num_heads, block_size, layout),
+                         word);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (s4[i] < 0) continue;
+            int64_t page, off;
+            split_slot(s4[i], block_size, log2_bs, page, off);
+            if (page >= num_blocks) continue;
+            uint8_t* scales = value_cache + page * page_stride + data_per_side;
+            scales[v_scale_offset(off, g, kS, h, num_heads, block_size, layout)] =
+                (uint8_t)(word >> (8 * i));
+          }
+        }
+      }
+    }
+    wave_sync();  // the next item rewrites this wave's LDS images
+  }
+}
+
+// --------------------------------------------------------------- generic kernel
 template <bool kF16>
 __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
     const uint16_t* __restrict__ key, int64_t key_row_stride, const uint16_t* __restrict__ value,
@@ -76,16 +350,7 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
     int64_t page_stride, int32_t layout, const float* __restrict__ k_scale,
     const float* __restrict__ v_scale, Div halves, Div scale_dim, Div quarter_s) {
   __shared__ float gs_over_m[2][16];  // RN(gs / M), M = 1..15, per side
-  const float gs_k = 1.0f / *k_scale;
-  const float gs_v = 1.0f / *v_scale;
-  if (threadIdx.x < 32) {
-    const int side = threadIdx.x >> 4, mm = threadIdx.x & 15;
-    gs_over_m[side][mm] = mm ? (side ? gs_v : gs_k) / (float)mm : 0.0f;
-  }
-  __syncthreads();
-  const bool table_k = gs_k >= 0x1p-100f && gs_k <= 0x1p100f;
-  const bool table_v = gs_v >= 0x1p-100f && gs_v <= 0x1p100f;
-  constexpr float kSixth = 1.0f / 6.0f;  // RN(1/6)
+  const GlobalScales G = load_global_scales(k_scale, v_scale, gs_over_m);
   const int32_t S = scale_dim.d;
   const int64_t data_dim = head_size / 2;
   const int64_t data_per_side = (int64_t)num_heads * block_size * data_dim;
@@ -115,7 +380,7 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
         slot[k] = slot_mapping[t];
         const uint16_t* src = (tk[k] & 1) ? value + t * value_row_stride
                                           : key + t * key_row_stride;
-        xv[k] = load_stream(reinterpret_cast<const u32x4*>(src + (int64_t)hq[k] * 8));
+        xv[k] = load_src(reinterpret_cast<const u32x4*>(src + (int64_t)hq[k] * 8));
       }
     }
     // ---- quantize and store (cross-lane steps run with every lane active)
@@ -123,17 +388,9 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
     for (int k = 0; k < kFp4Unroll; ++k) {
       float x[8];
       unpack8_src<kF16>(xv[k], x);
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[i]));
-      m = max(m, dpp<kQuadSwap1>(m));  // the other half of the block
       const int kv = tk[k] & 1;
-      const float gs = kv ? gs_v : gs_k;
-      const float amax = __uint_as_float(m);
-      const float t6 = amax * gs;
-      const float q6 = t6 * kSixth;
-      const float sf = __builtin_fmaf(__builtin_fmaf(-q6, 6.0f, t6), kSixth, q6);  // = t6 / 6
-      const uint32_t sf8 = e4m3_pack2<false>(fminf(sf, 448.0f), 0.0f, 0u) & 0xffu;
+      uint32_t sf8;
+      const uint32_t packed = nvfp4_half_block(x, G.gs(kv), G.table(kv), gs_over_m[kv], sf8);
       // K: scale bytes of blocks g..g+3 (lanes +0, +2, +4, +6) in one dword
       const uint32_t sf_word = sf8 | (from_lane_above<2>(sf8) << 8) |
                                (from_lane_above<4>(sf8) << 16) | (from_lane_above<6>(sf8) << 24);
@@ -142,29 +399,14 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
       split_slot(slot[k], block_size, log2_bs, page, off);
       if (page >= num_blocks) continue;
 
-      // decode(sf8) = M * 2^p: normal codes M = 8 + mantissa, p = exponent - 10;
-      // subnormal codes M = mantissa, p = -9
-      const uint32_t ex = sf8 >> 3;
-      const uint32_t mm = ex ? 8u + (sf8 & 7u) : (sf8 & 7u);
-      const int p = ex ? (int)ex - 10 : -9;
-      float r;
-      if (kv ? table_v : table_k)
-        r = sf8 ? __builtin_ldexpf(gs_over_m[kv][mm], -p) : 0.0f;
-      else
-        r = sf8 ? gs / e4m3_decode(sf8) : 0.0f;
-      uint32_t packed = e2m1_pack2<0>(x[0] * r, x[1] * r, 0u);
-      packed = e2m1_pack2<1>(x[2] * r, x[3] * r, packed);
-      packed = e2m1_pack2<2>(x[4] * r, x[5] * r, packed);
-      packed = e2m1_pack2<3>(x[6] * r, x[7] * r, packed);
-
       const uint32_t half = hq[k] & 1;
       uint32_t h, g;
       scale_dim.split(hq[k] >> 1, h, g);
       uint8_t* side = (kv ? value_cache : key_cache) + page * page_stride;
       int64_t data_off;
-      if (layout == 0)  // HND
+      if (layout == PKV_LAYOUT_HND)
         data_off = ((int64_t)h * block_size + off) * data_dim + (int64_t)g * 8 + half * 4;
-      else              // NHD
+      else
         data_off = (off * num_heads + h) * data_dim + (int64_t)g * 8 + half * 4;
       *reinterpret_cast<uint32_t*>(side + data_off) = packed;
 
@@ -172,18 +414,13 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
       uint8_t* scales = side + data_per_side;
       if (kv == 0) {
         if ((g & 3) == 0) {
-          const int64_t row_off = layout == 0 ? ((int64_t)h * block_size + off) * S
-                                              : (off * num_heads + h) * S;
+          const int64_t row_off = layout == PKV_LAYOUT_HND ? ((int64_t)h * block_size + off) * S
+                                                           : (off * num_heads + h) * S;
           *reinterpret_cast<uint32_t*>(scales + row_off + g) = sf_word;
         }
       } else {  // V scales: 4x4-tile swizzle of the per-head [B, S] tile
-        uint32_t gq, gr;
-        quarter_s.split(g, gq, gr);  // g / (S/4), g % (S/4)
-        const int64_t row = (off >> 2) * 4 + gq;
-        const int64_t col = (int64_t)gr * 4 + (off & 3);
-        const int64_t so = layout == 0 ? ((int64_t)h * block_size + row) * S + col
-                                       : (row * num_heads + h) * S + col;
-        scales[so] = (uint8_t)sf8;
+        scales[v_scale_offset(off, (int32_t)g, S, (int32_t)h, num_heads, block_size, layout)] =
+            (uint8_t)sf8;
       }
     }
   }
@@ -196,9 +433,26 @@ int32_t log2_exact(int64_t v) {
   return l;
 }
 
-}  // namespace
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream) {
+template <int kD>
+int launch_tile(const StoreFp4Args& a, hipStream_t stream) {
+  const int64_t tiles = (a.num_tokens + kFp4Tile - 1) / kFp4Tile;
+  const int64_t items = tiles * 2 * a.num_heads;
+  const int64_t logical = (items + kFp4Waves - 1) / kFp4Waves;
+  int64_t blocks = logical < kFp4MaxBlocks ? logical : kFp4MaxBlocks;
+  blocks = (blocks + kNumXcd - 1) / kNumXcd * kNumXcd;  // whole XCD ranges
+  auto kernel = a.src_dtype == PKV_DTYPE_F16 ? store_kv_fp4_tile_kernel<kD, true>
+                                             : store_kv_fp4_tile_kernel<kD, false>;
+  hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kFp4Threads), 0, stream, a.key,
+                     a.key_row_stride, a.value, a.value_row_stride, a.key_cache, a.value_cache,
+                     a.slot_mapping, a.num_tokens, items, logical, a.num_heads, a.block_size,
+                     a.log2_block_size, a.num_blocks, a.page_stride, a.layout, a.k_scale,
+                     a.v_scale);
+  return (int)hipGetLastError();
+}
+
+int launch_generic(const StoreFp4Args& a, hipStream_t stream) {
   const int32_t S = a.head_size / 16;
   const int64_t halves = 2 * (int64_t)a.num_heads * S;  // half-blocks per token side
   const Div halves_div{(int32_t)halves, log2_exact(halves)};
@@ -223,6 +477,22 @@ int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream) {
     if (e != hipSuccess) return (int)e;
   }
   return 0;
+}
+
+}  // namespace
+
+#ifndef PKV_FP4_MODE
+#define PKV_FP4_MODE 0  // 0: tile kernel where it applies, 1: always the generic kernel
+#endif
+
+int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream) {
+  const bool sides16 = aligned16(a.key_cache) && aligned16(a.value_cache) && a.page_stride % 16 == 0;
+  if (PKV_FP4_MODE == 0 && sides16) {
+    if (a.head_size == 64) return launch_tile<64>(a, stream);
+    if (a.head_size == 128) return launch_tile<128>(a, stream);
+    if (a.head_size == 256) return launch_tile<256>(a, stream);
+  }
+  return launch_generic(a, stream);
 }
 
 }  // namespace pkv

@@ -470,3 +470,56 @@ def test_store_fp4_f16_shapes_and_edges():
     x[3] = np.float32(65504.0)
     x[3, :, :, 1::2] = -3.0
     run_store4(f, key_bits=workloads.f16_bits(x.reshape(48, -1)))
+
+
+# Slots that fill pages as a prefill does: runs of consecutive slots, so the
+# NVFP4 store writes whole page lines and whole 4-token V-scale tiles; the
+# request lengths (not multiples of 4 or 16) and dropped slots make tiles
+# that straddle pages, partial swizzle tiles and ragged tails.
+@pytest.mark.parametrize("lens,H,D,B,layout,drop,dtype", [
+    ([37, 5, 16, 100, 1, 64], 2, 128, 16, 0, 0.0, "bf16"),
+    ([37, 5, 16, 100, 1, 64], 2, 128, 16, 1, 0.05, "bf16"),
+    ([40, 24, 3, 96], 3, 64, 8, 0, 0.1, "f16"),
+    ([200, 17, 33], 1, 256, 32, 0, 0.02, "bf16"),
+    ([200, 17, 33], 2, 256, 32, 1, 0.0, "f16"),
+    ([48, 48, 13, 50], 4, 128, 12, 0, 0.05, "bf16"),
+    ([1000, 1000, 1000], 8, 128, 16, 0, 0.0, "bf16"),
+])
+def test_store_fp4_paged_slots(lens, H, D, B, layout, drop, dtype):
+    banner(f"nvfp4 paged slots lens={lens} H={H} D={D} B={B} layout={layout} drop={drop} {dtype}")
+    f = workloads.paged_fp4(sum(lens) + H + D + B, lens, H=H, D=D, B=B, layout=layout,
+                            drop_frac=drop, dtype=dtype)
+    run_store4(f)
+
+
+@pytest.mark.parametrize("D,layout", [(128, 0), (128, 1), (64, 0), (256, 1)])
+def test_store_fp4_sides_8_byte_aligned(D, layout):
+    """Page sides that are 8- but not 16-byte aligned (page stride = two sides
+    + 8 bytes, buffer offset 8): the store still writes exactly the oracle's
+    bytes and leaves the 8 padding bytes of every page untouched."""
+    banner(f"nvfp4 8-byte aligned sides D={D} layout={layout}")
+    H, B = 2, 16
+    f = workloads.paged_fp4(77 + D + layout, [45, 19, 64], H=H, D=D, B=B, layout=layout)
+    nb, side = f.cache_init.shape[0], f.cache_init.shape[2]
+    stride = 2 * side + 8
+    rng = np.random.default_rng(5)
+    flat = rng.integers(0, 256, size=8 + nb * stride, dtype=np.uint8)
+    pages = flat[8:].reshape(nb, stride)
+    pages[:, :2 * side] = f.cache_init.reshape(nb, 2 * side)
+    ref_pages = pages.copy()
+    ref = f.cache_init.copy()
+    oracle.store_kv_fp4(f.key_bits, f.value_bits, ref, f.slot_mapping, H, D, B, layout,
+                        f.k_scale, f.v_scale, dtype=f.dtype)
+    ref_pages[:, :2 * side] = ref.reshape(nb, 2 * side)
+    buf = dev(flat)
+    view = buf[8:].view(nb, stride)
+    T = f.slot_mapping.shape[0]
+    shape = (T, H, D)
+    pkv.pkv_store_kv_fp4(bf16_dev(f.key_bits, shape, f.dtype), bf16_dev(f.value_bits, shape, f.dtype),
+                         view[:, :side], view[:, side:2 * side], dev(f.slot_mapping),
+                         torch.tensor([f.k_scale], dtype=torch.float32, device=DEV),
+                         torch.tensor([f.v_scale], dtype=torch.float32, device=DEV),
+                         block_size=B, layout=layout)
+    out = host(buf)
+    np.testing.assert_array_equal(out[:8], flat[:8])
+    np.testing.assert_array_equal(out[8:].reshape(nb, stride), ref_pages)

@@ -266,6 +266,17 @@ def small_fp4(seed, T, H=2, D=64, B=8, num_blocks=None, layout=0, drop_frac=0.1,
                 drop_frac=drop_frac, dtype=dtype)
 
 
+def paged_fp4(seed, lens, H=2, D=128, B=16, layout=0, drop_frac=0.05, dtype="bf16",
+              spare_pages=3) -> Fp4Workload:
+    """NVFP4 store inputs whose slots fill pages the way a prefill does: each
+    request (token counts `lens`, in order) owns whole pages from a seeded
+    shuffle, token i of a request in slot page*B + i%B; then a fraction
+    `drop_frac` of the slots is set to -1."""
+    need = sum(-(-n // B) for n in lens)
+    return _fp4(f"paged_fp4_{seed}", seed, None, H, D, B, need + spare_pages, layout=layout,
+                lens=list(lens), drop_frac=drop_frac, dtype=dtype)
+
+
 def prefill_fp4(num_reqs=256, req_len=1000, H=8, D=128, B=16, seed=1005) -> Fp4Workload:
     """The 256 x 1000-token prefill batch through the NVFP4 K/V store
     (H=8, D=128, B=16); every request owns whole pages from a seeded shuffle."""
