@@ -28,14 +28,20 @@ namespace pkv {
 
 namespace {
 
-constexpr int kStoreThreads = 256;
+#ifndef PKV_STORE8_THREADS
+#define PKV_STORE8_THREADS 256
+#endif
+constexpr int kStoreThreads = PKV_STORE8_THREADS;
 
 #ifndef PKV_STORE8_UNROLL
-#define PKV_STORE8_UNROLL 1
+#define PKV_STORE8_UNROLL 2
 #endif
 constexpr int kStoreUnroll = PKV_STORE8_UNROLL;  // token groups per wave in flight
 #ifndef PKV_STORE8_NT
-#define PKV_STORE8_NT 0  // nontemporal code and scale stores
+#define PKV_STORE8_NT 0  // nontemporal code stores
+#endif
+#ifndef PKV_STORE8_NT_SCALE
+#define PKV_STORE8_NT_SCALE 0  // nontemporal scale stores
 #endif
 
 // kLanes lanes per token (a power of two), each holding kChunks runs of 8
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
     }
     if (part == 0) {
       float* dst = reinterpret_cast<float*>(page_base + (int64_t)block_size * head_dim + off * 4);
-      if constexpr (PKV_STORE8_NT) __builtin_nontemporal_store(s, dst);
+      if constexpr (PKV_STORE8_NT_SCALE) __builtin_nontemporal_store(s, dst);
       else *dst = s;
     }
   }

@@ -55,7 +55,10 @@ namespace pkv {
 
 namespace {
 
-constexpr int kFp4Threads = 256;
+#ifndef PKV_FP4_THREADS
+#define PKV_FP4_THREADS 256
+#endif
+constexpr int kFp4Threads = PKV_FP4_THREADS;
 constexpr int kFp4Waves = kFp4Threads / kWave;
 
 #ifndef PKV_FP4_UNROLL
@@ -63,7 +66,14 @@ constexpr int kFp4Waves = kFp4Threads / kWave;
 #endif
 constexpr int kFp4Unroll = PKV_FP4_UNROLL;  // half-blocks per lane in flight (generic kernel)
 
-constexpr int kFp4Tile = 16;  // tokens per wave item (tile kernel)
+#ifndef PKV_FP4_TILE
+#define PKV_FP4_TILE 16
+#endif
+constexpr int kFp4Tile = PKV_FP4_TILE;  // tokens per wave item (tile kernel)
+#ifndef PKV_FP4_ITEMS
+#define PKV_FP4_ITEMS 1
+#endif
+constexpr int kFp4Items = PKV_FP4_ITEMS;  // items per wave whose loads are in flight together
 
 #ifndef PKV_FP4_NT_STORE
 #define PKV_FP4_NT_STORE 1
@@ -210,133 +220,148 @@ void store_kv_fp4_tile_kernel(
   static_assert(kScaleWords <= kWave && kS % 4 == 0, "scale words per lane");
 
   __shared__ float gs_over_m[2][16];
-  __shared__ __align__(16) uint32_t data_img[kFp4Waves][kDataBytes / 4];
-  __shared__ __align__(16) uint32_t scale_img[kFp4Waves][kScaleWords];
+  __shared__ __align__(16) uint32_t data_img[kFp4Waves][kFp4Items][kDataBytes / 4];
+  __shared__ __align__(16) uint32_t scale_img[kFp4Waves][kFp4Items][kScaleWords];
   const GlobalScales G = load_global_scales(k_scale, v_scale, gs_over_m);
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
-  uint32_t* dimg = data_img[wave];
-  uint32_t* simg = scale_img[wave];
-  uint8_t* simg8 = reinterpret_cast<uint8_t*>(simg);
+  const int c = lane % kC;  // source chunk this lane loads, in every load
   const int64_t data_per_side = (int64_t)num_heads * block_size * (kD / 2);
   const int32_t sides_heads = 2 * num_heads;
 
-  for (int64_t lb = xcd_contiguous_block(); lb < num_logical_blocks; lb += gridDim.x) {
-    const int64_t item = lb * kFp4Waves + wave;  // (tile, side, head)
-    if (item >= num_items) continue;
-    const int64_t tile = item / sides_heads;
-    const int32_t sh = (int32_t)(item - tile * sides_heads);
-    const int kv = sh >= num_heads;
-    const int32_t h = kv ? sh - num_heads : sh;
-    const int64_t t0 = tile * kFp4Tile;
-    const uint16_t* src = kv ? value : key;
-    const int64_t row_stride = kv ? value_row_stride : key_row_stride;
-
-    // slot of token t0 + (lane % 16); tokens past the end have slot -1
-    const int64_t my_t = t0 + (lane & (kFp4Tile - 1));
-    const int64_t my_slot = my_t < num_tokens ? slot_mapping[my_t] : -1;
-
-    // ---- loads: lane holds chunk c of token tk for each of kLoads loads
-    const int c = lane % kC;
-    u32x4 xv[kLoads];
+#ifndef PKV_FP4_XCD
+#define PKV_FP4_XCD 1
+#endif
+  const int64_t first_block = PKV_FP4_XCD ? xcd_contiguous_block() : blockIdx.x;
+  for (int64_t lb = first_block; lb < num_logical_blocks; lb += gridDim.x) {
+    // this wave's kFp4Items consecutive items, each a (tile, side, head)
+    int64_t t0[kFp4Items], my_slot[kFp4Items];
+    int kv[kFp4Items];
+    int32_t h[kFp4Items];
+    bool valid[kFp4Items];
+    u32x4 xv[kFp4Items][kLoads];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int64_t t = t0 + k * kTokPerLoad + lane / kC;
-      xv[k] = u32x4{0u, 0u, 0u, 0u};
-      if (t < num_tokens)
-        xv[k] = load_src(reinterpret_cast<const u32x4*>(src + t * row_stride + (int64_t)h * kD) + c);
-    }
-
-    // ---- quantize into the LDS images (codes [tok][kD/2]; K scales
-    // [tok][kS]; V scales [tok/4][g][tok%4], i.e. the swizzled order)
-    const float gs = G.gs(kv);
-    const bool table = G.table(kv);
+    for (int u = 0; u < kFp4Items; ++u) {
+      const int64_t item = (lb * kFp4Waves + wave) * kFp4Items + u;
+      valid[u] = item < num_items;  // wave-uniform
+      const int64_t tile = item / sides_heads;
+      const int32_t sh = (int32_t)(item - tile * sides_heads);
+      kv[u] = sh >= num_heads;
+      h[u] = kv[u] ? sh - num_heads : sh;
+      t0[u] = tile * kFp4Tile;
+      // slot of token t0 + (lane % 16); tokens past the end have slot -1
+      const int64_t my_t = t0[u] + (lane & (kFp4Tile - 1));
+      my_slot[u] = valid[u] && my_t < num_tokens ? slot_mapping[my_t] : -1;
+      // loads: lane holds chunk c of token k * kTokPerLoad + lane / kC
+      const uint16_t* src = kv[u] ? value : key;
+      const int64_t row_stride = kv[u] ? value_row_stride : key_row_stride;
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int tk = k * kTokPerLoad + lane / kC;
-      float x[8];
-      unpack8_src<kF16>(xv[k], x);
-      uint32_t sf8;
-      const uint32_t packed = nvfp4_half_block(x, gs, table, gs_over_m[kv], sf8);
-      dimg[tk * kC + c] = packed;  // byte offset tk*kD/2 + 4c
-      if ((c & 1) == 0) {
-        const int g = c >> 1;
-        const int pos = kv ? (tk >> 2) * 4 * kS + g * 4 + (tk & 3) : tk * kS + g;
-        simg8[pos] = (uint8_t)sf8;
+      for (int k = 0; k < kLoads; ++k) {
+        const int64_t t = t0[u] + k * kTokPerLoad + lane / kC;
+        xv[u][k] = u32x4{0u, 0u, 0u, 0u};
+        if (valid[u] && t < num_tokens)
+          xv[u][k] = load_src(
+              reinterpret_cast<const u32x4*>(src + t * row_stride + (int64_t)h[u] * kD) + c);
       }
     }
-    wave_sync();
 
-    // ---- code bytes: 16 bytes per lane, address from the chunk's token slot
 #pragma unroll
-    for (int q0 = 0; q0 < kDataChunks; q0 += kWave) {
-      const int q = q0 + lane;
-      const int tok = (q < kDataChunks ? q : 0) / kChunksPerTok;
-      const int64_t slot = lane_value(my_slot, tok);
-      if (q < kDataChunks && slot >= 0) {
-        int64_t page, off;
-        split_slot(slot, block_size, log2_bs, page, off);
-        if (page < num_blocks) {
-          uint8_t* side = (kv ? value_cache : key_cache) + page * page_stride;
-          const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h * block_size + off
-                                                       : off * num_heads + h;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(dimg + 4 * q);
-          store_codes16(side + row * (kD / 2) + (q % kChunksPerTok) * 16, v);
+    for (int u = 0; u < kFp4Items; ++u) {
+      if (!valid[u]) continue;
+      uint32_t* dimg = data_img[wave][u];
+      uint32_t* simg = scale_img[wave][u];
+      uint8_t* simg8 = reinterpret_cast<uint8_t*>(simg);
+      // ---- quantize into the LDS images (codes [tok][kD/2]; K scales
+      // [tok][kS]; V scales [tok/4][g][tok%4], i.e. the swizzled order)
+      const float gs = G.gs(kv[u]);
+      const bool table = G.table(kv[u]);
+#pragma unroll
+      for (int k = 0; k < kLoads; ++k) {
+        const int tk = k * kTokPerLoad + lane / kC;
+        float x[8];
+        unpack8_src<kF16>(xv[u][k], x);
+        uint32_t sf8;
+        const uint32_t packed = nvfp4_half_block(x, gs, table, gs_over_m[kv[u]], sf8);
+        dimg[tk * kC + c] = packed;  // byte offset tk*kD/2 + 4c
+        if ((c & 1) == 0) {
+          const int g = c >> 1;
+          const int pos = kv[u] ? (tk >> 2) * 4 * kS + g * 4 + (tk & 3) : tk * kS + g;
+          simg8[pos] = (uint8_t)sf8;
         }
       }
-    }
+      wave_sync();
 
-    // ---- scale bytes: one dword per lane
-    const int sw = lane < kScaleWords ? lane : 0;
-    const uint32_t word = simg[sw];
-    if (kv == 0) {
-      const int tok = (4 * sw) / kS;
-      const int64_t slot = lane_value(my_slot, tok);
-      if (lane < kScaleWords && slot >= 0) {
-        int64_t page, off;
-        split_slot(slot, block_size, log2_bs, page, off);
-        if (page < num_blocks) {
-          uint8_t* scales = key_cache + page * page_stride + data_per_side;
-          const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h * block_size + off
-                                                       : off * num_heads + h;
-          store_scale4(scales + row * kS + (4 * sw) % kS, word);
-        }
-      }
-    } else {
-      // dword sw = block g of the 4 tokens 4*quad .. 4*quad+3
-      const int quad = sw / kS, g = sw % kS;
-      int64_t s4[4];
+      // ---- code bytes: 16 bytes per lane, address from the chunk's token slot
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] = lane_value(my_slot, 4 * quad + i);
-      if (lane < kScaleWords) {
-        const bool whole = s4[0] >= 0 && (s4[0] & 3) == 0 && s4[1] == s4[0] + 1 &&
-                           s4[2] == s4[0] + 2 && s4[3] == s4[0] + 3;
-        if (whole) {
-          // 4 consecutive slots starting at a multiple of 4: one page (block
-          // sizes are multiples of 4), one swizzle tile, one dword
+      for (int q0 = 0; q0 < kDataChunks; q0 += kWave) {
+        const int q = q0 + lane;
+        const int tok = (q < kDataChunks ? q : 0) / kChunksPerTok;
+        const int64_t slot = lane_value(my_slot[u], tok);
+        if (q < kDataChunks && slot >= 0) {
           int64_t page, off;
-          split_slot(s4[0], block_size, log2_bs, page, off);
+          split_slot(slot, block_size, log2_bs, page, off);
           if (page < num_blocks) {
-            uint8_t* scales = value_cache + page * page_stride + data_per_side;
-            store_scale4(scales + v_scale_offset(off, g, kS, h, num_heads, block_size, layout),
-                         word);
+            uint8_t* side = (kv[u] ? value_cache : key_cache) + page * page_stride;
+            const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h[u] * block_size + off
+                                                         : off * num_heads + h[u];
+            const u32x4 v = *reinterpret_cast<const u32x4*>(dimg + 4 * q);
+            store_codes16(side + row * (kD / 2) + (q % kChunksPerTok) * 16, v);
           }
-        } else {
+        }
+      }
+
+      // ---- scale bytes: one dword per lane
+      const int sw = lane < kScaleWords ? lane : 0;
+      const uint32_t word = simg[sw];
+      if (kv[u] == 0) {
+        const int tok = (4 * sw) / kS;
+        const int64_t slot = lane_value(my_slot[u], tok);
+        if (lane < kScaleWords && slot >= 0) {
+          int64_t page, off;
+          split_slot(slot, block_size, log2_bs, page, off);
+          if (page < num_blocks) {
+            uint8_t* scales = key_cache + page * page_stride + data_per_side;
+            const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h[u] * block_size + off
+                                                         : off * num_heads + h[u];
+            store_scale4(scales + row * kS + (4 * sw) % kS, word);
+          }
+        }
+      } else {
+        // dword sw = block g of the 4 tokens 4*quad .. 4*quad+3
+        const int quad = sw / kS, g = sw % kS;
+        int64_t s4[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (s4[i] < 0) continue;
+        for (int i = 0; i < 4; ++i) s4[i] = lane_value(my_slot[u], 4 * quad + i);
+        if (lane < kScaleWords) {
+          const bool whole = s4[0] >= 0 && (s4[0] & 3) == 0 && s4[1] == s4[0] + 1 &&
+                             s4[2] == s4[0] + 2 && s4[3] == s4[0] + 3;
+          if (whole) {
+            // 4 consecutive slots starting at a multiple of 4: one page (block
+            // sizes are multiples of 4), one swizzle tile, one dword
             int64_t page, off;
-            split_slot(s4[i], block_size, log2_bs, page, off);
-            if (page >= num_blocks) continue;
-            uint8_t* scales = value_cache + page * page_stride + data_per_side;
-            scales[v_scale_offset(off, g, kS, h, num_heads, block_size, layout)] =
-                (uint8_t)(word >> (8 * i));
+            split_slot(s4[0], block_size, log2_bs, page, off);
+            if (page < num_blocks) {
+              uint8_t* scales = value_cache + page * page_stride + data_per_side;
+              store_scale4(
+                  scales + v_scale_offset(off, g, kS, h[u], num_heads, block_size, layout), word);
+            }
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (s4[i] < 0) continue;
+              int64_t page, off;
+              split_slot(s4[i], block_size, log2_bs, page, off);
+              if (page >= num_blocks) continue;
+              uint8_t* scales = value_cache + page * page_stride + data_per_side;
+              scales[v_scale_offset(off, g, kS, h[u], num_heads, block_size, layout)] =
+                  (uint8_t)(word >> (8 * i));
+            }
           }
         }
       }
     }
-    wave_sync();  // the next item rewrites this wave's LDS images
+    wave_sync();  // the next iteration rewrites this wave's LDS images
   }
 }
 
@@ -439,7 +464,7 @@ template <int kD>
 int launch_tile(const StoreFp4Args& a, hipStream_t stream) {
   const int64_t tiles = (a.num_tokens + kFp4Tile - 1) / kFp4Tile;
   const int64_t items = tiles * 2 * a.num_heads;
-  const int64_t logical = (items + kFp4Waves - 1) / kFp4Waves;
+  const int64_t logical = (items + kFp4Waves * kFp4Items - 1) / (kFp4Waves * kFp4Items);
   int64_t blocks = logical < kFp4MaxBlocks ? logical : kFp4MaxBlocks;
   blocks = (blocks + kNumXcd - 1) / kNumXcd * kNumXcd;  // whole XCD ranges
   auto kernel = a.src_dtype == PKV_DTYPE_F16 ? store_kv_fp4_tile_kernel<kD, true>
