@@ -23,7 +23,8 @@ writes 0.3 GB of pages per step.
 
 Printed: one JSON line.  `value` = algorithmic bytes of one step / measured
 step time (GB/s); per-kernel durations come from HIP events recorded on the
-launch stream around each launch; `roofline` describes the kernel with the
+launch stream around each launch (timing-only events, without the cache
+write-back a default event performs); `roofline` describes the kernel with the
 longest average duration; `cpu_baseline` times the CPU oracle on the same
 batch (one thread).
 """
@@ -87,6 +88,63 @@ def parse_args():
                    help="run a plain 256 MiB fp32 copy-like kernel (torch.neg) before the "
                         "timed steps, for scaling hardware byte counters")
     return p.parse_args()
+
+
+class HipTimingEvents:
+    """HIP events for timing only, on the HIP runtime torch has loaded.
+
+    They are created with hipEventDisableSystemFence: recording one then does
+    not write back and invalidate the caches, which torch's events do and
+    which would add that cost to the kernel timed before it and to the one
+    after it.  A timed step therefore runs like an untimed one."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
+
+    def __init__(self):
+        import ctypes
+        paths = set()
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+        if len(paths) != 1:
+            raise RuntimeError(f"expected one loaded HIP runtime, found {sorted(paths)}")
+        self._ct = ctypes
+        hip = ctypes.CDLL(paths.pop())
+        P = ctypes.c_void_p
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(P), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [P, P]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), P, P]
+        hip.hipEventDestroy.argtypes = [P]
+        for fn in ("hipEventCreateWithFlags", "hipEventRecord", "hipEventElapsedTime",
+                   "hipEventDestroy"):
+            getattr(hip, fn).restype = ctypes.c_int
+        self._hip = hip
+        self._events = []
+
+    def _ok(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def create(self):
+        ev = self._ct.c_void_p()
+        self._ok(self._hip.hipEventCreateWithFlags(self._ct.byref(ev), self.DISABLE_SYSTEM_FENCE),
+                 "hipEventCreateWithFlags")
+        self._events.append(ev)
+        return ev
+
+    def record(self, ev, stream_handle):
+        self._ok(self._hip.hipEventRecord(ev, self._ct.c_void_p(stream_handle)), "hipEventRecord")
+
+    def elapsed_ms(self, a, b):
+        ms = self._ct.c_float()
+        self._ok(self._hip.hipEventElapsedTime(self._ct.byref(ms), a, b), "hipEventElapsedTime")
+        return ms.value
+
+    def destroy_all(self):
+        for ev in self._events:
+            self._hip.hipEventDestroy(ev)
+        self._events = []
 
 
 def algorithmic_bytes(T, D, H4, D4, R, maxb):
@@ -171,22 +229,25 @@ def main():
 
     lag = len(sets) // 2  # the gather reads pages stored `lag` steps earlier
 
+    timing = HipTimingEvents()
+    stream = torch.cuda.current_stream().cuda_stream  # every launch goes to this stream
+
+    def mark(ev, j):
+        if ev is not None:
+            timing.record(ev[j], stream)
+
     def step(i, ev=None):
         s = sets[i % len(sets)]
         sg = sets[(i - lag) % len(sets)]
-        if ev is not None:
-            ev[0].record()
+        mark(ev, 0)
         pkv.pkv_store_indexer_k_fp8(s["k"], s["slot"], s["cache"], block_size=w.block_size)
-        if ev is not None:
-            ev[1].record()
+        mark(ev, 1)
         pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slot4, k4s, v4s,
                              block_size=f.block_size, layout=f.layout)
-        if ev is not None:
-            ev[2].record()
+        mark(ev, 2)
         pkv.pkv_gather_indexer_k_fp8(sg["cache"], sg["kf"], sg["ks"], bt, cu,
                                      block_size=w.block_size)
-        if ev is not None:
-            ev[3].record()
+        mark(ev, 3)
 
     if args.calibration_copy:
         src = torch.randn(64 << 20, device=dev)          # 256 MiB fp32
@@ -201,7 +262,7 @@ def main():
     # default warmup (~30 ms of steps) runs past the clock transient that the
     # first few dozen launches of the step show, so the timed steps measure the
     # sustained rate.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    events = [[timing.create() for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -214,8 +275,9 @@ def main():
     per_kernel_ms = {n: 0.0 for n in names}
     for ev in events:
         for j, n in enumerate(names):
-            per_kernel_ms[n] += ev[j].elapsed_time(ev[j + 1])
+            per_kernel_ms[n] += timing.elapsed_ms(ev[j], ev[j + 1])
     per_kernel_ms = {n: v / args.steps for n, v in per_kernel_ms.items()}
+    timing.destroy_all()
     ms_per_step = wall * 1e3 / args.steps
 
     alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
