@@ -74,6 +74,20 @@ def _load():
     lib.oracle_store_kv_fp4.argtypes = [P, i64, P, i64, i32, P, P, P, i64, i32, i32, i32,
                                         i64, i64, i32, f32, f32]
     lib.oracle_store_kv_fp4.restype = None
+    lib.oracle_f32_to_bf16.argtypes = [f32]
+    lib.oracle_f32_to_bf16.restype = u16
+    lib.oracle_f32_to_f16.argtypes = [f32]
+    lib.oracle_f32_to_f16.restype = u16
+    lib.oracle_f32_to_bf16_array.argtypes = [P, P, i64]
+    lib.oracle_f32_to_bf16_array.restype = None
+    lib.oracle_f32_to_f16_array.argtypes = [P, P, i64]
+    lib.oracle_f32_to_f16_array.restype = None
+    lib.oracle_gather_indexer_k_dequant.argtypes = [P, P, i64, i32, P, P, i32, i32, i64, i64,
+                                                    i64, i32, i32]
+    lib.oracle_gather_indexer_k_dequant.restype = None
+    lib.oracle_gather_kv_fp4_dequant.argtypes = [P, P, P, i64, P, i64, i32, P, P, i32, i32,
+                                                 i64, i32, i32, i32, i64, i64, i32, f32, f32]
+    lib.oracle_gather_kv_fp4_dequant.restype = None
     _lib = lib
     return lib
 
@@ -194,3 +208,64 @@ def store_kv_fp4(key_bits, value_bits, kv_cache, slot_mapping, num_heads, head_s
         SRC_DTYPES[dtype], _ptr(kv_cache), _ptr(kv_cache, side_bytes), _ptr(slot_mapping), T,
         num_heads, head_size, block_size, kv_cache.shape[0], page_stride, layout,
         float(k_scale), float(v_scale))
+
+
+# ----------------------------------------------------------------- reader side
+OUT_DTYPES = {"bf16": 0, "f16": 1}
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """binary32 -> bf16 bit patterns, round to nearest even; elementwise."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_f32_to_bf16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def f32_to_f16(x) -> np.ndarray:
+    """binary32 -> binary16 bit patterns, round to nearest even; elementwise."""
+    x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_f32_to_f16_array(_ptr(x), _ptr(out), x.size)
+    return out
+
+
+def gather_indexer_k_dequant(kv_cache, out, block_table, cu_seq_lens, block_size, head_dim,
+                             dtype="bf16"):
+    """Gather and dequantise into out (uint16 patterns [T, >=D], bf16 or f16; in place)."""
+    _need(kv_cache, np.uint8, "kv_cache")
+    _need(out, np.uint16, "out")
+    _need(block_table, np.int32, "block_table")
+    _need(cu_seq_lens, np.int32, "cu_seq_lens")
+    num_reqs, maxb = block_table.shape
+    assert cu_seq_lens.shape == (num_reqs + 1,)
+    assert out.ndim == 2 and out.shape[1] >= head_dim
+    _load().oracle_gather_indexer_k_dequant(
+        _ptr(kv_cache), _ptr(out), out.shape[1], OUT_DTYPES[dtype], _ptr(block_table),
+        _ptr(cu_seq_lens), num_reqs, maxb, out.shape[0], kv_cache.shape[0], kv_cache.shape[1],
+        block_size, head_dim)
+
+
+def gather_kv_fp4_dequant(kv_cache, key_out, value_out, block_table, cu_seq_lens, num_heads,
+                          head_size, block_size, layout, k_scale, v_scale, dtype="bf16"):
+    """NVFP4 pages back to bf16 or f16 K/V rows (uint16 patterns [T, >=H*D]; in place).
+
+    kv_cache: uint8 [num_blocks, 2, side_bytes]; side 0 holds K, side 1 holds V.
+    """
+    _need(kv_cache, np.uint8, "kv_cache")
+    _need(key_out, np.uint16, "key_out")
+    _need(value_out, np.uint16, "value_out")
+    _need(block_table, np.int32, "block_table")
+    _need(cu_seq_lens, np.int32, "cu_seq_lens")
+    assert kv_cache.ndim == 3 and kv_cache.shape[1] == 2
+    num_reqs, maxb = block_table.shape
+    assert cu_seq_lens.shape == (num_reqs + 1,)
+    T = key_out.shape[0]
+    assert value_out.shape[0] == T
+    assert key_out.shape[1] >= num_heads * head_size and value_out.shape[1] >= num_heads * head_size
+    side_bytes = kv_cache.shape[2]
+    _load().oracle_gather_kv_fp4_dequant(
+        _ptr(kv_cache), _ptr(kv_cache, side_bytes), _ptr(key_out), key_out.shape[1],
+        _ptr(value_out), value_out.shape[1], OUT_DTYPES[dtype], _ptr(block_table),
+        _ptr(cu_seq_lens), num_reqs, maxb, T, num_heads, head_size, block_size,
+        kv_cache.shape[0], 2 * side_bytes, layout, float(k_scale), float(v_scale))

@@ -387,3 +387,229 @@ void oracle_store_kv_fp4(const uint16_t *key, int64_t key_row_stride,
         }
     }
 }
+
+/* ================================================================== */
+/* Reader side: dequantising gathers.                                   */
+/* ================================================================== */
+
+/* binary32 -> bf16, round to nearest, ties to even.  bf16 keeps the top  */
+/* 16 bits of the binary32 pattern; the result is the nearer of the two   */
+/* bf16 values around x (by magnitude), the one with an even last kept bit */
+/* on a tie; values past the largest finite bf16 by half an ulp or more    */
+/* become infinity.  NaN stays NaN (quiet, sign kept).  Worked in binary64 */
+/* on the magnitude, where every step is exact except rint().              */
+uint16_t oracle_f32_to_bf16(float x)
+{
+    uint32_t bits;
+    uint16_t sign;
+    double a, ulp, q;
+    int e;
+    memcpy(&bits, &x, 4);
+    sign = (uint16_t)((bits >> 16) & 0x8000);
+    if (isnan(x))
+        return sign | 0x7FC0;
+    a = fabs((double)x);
+    if (isinf(x))
+        return sign | 0x7F80;
+    if (a == 0.0)
+        return sign;
+    /* bf16 has 8 significant bits and binary32's exponent range: the ulp */
+    /* of a normal value in [2^e, 2^(e+1)) is 2^(e-7); subnormals (below   */
+    /* 2^-126) have ulp 2^-133.                                            */
+    e = ilogb(a);
+    if (e < -126)
+        e = -126;
+    ulp = ldexp(1.0, e - 7);
+    q = rint(a / ulp) * ulp;          /* nearest multiple of the ulp, ties even */
+    if (q > 0x1.FEp127)               /* past the largest finite bf16, 0x7F7F */
+        return sign | 0x7F80;
+    {
+        float qf = (float)q;         /* exact: q has at most 8 significant bits */
+        uint32_t qb;
+        memcpy(&qb, &qf, 4);
+        return sign | (uint16_t)((qb >> 16) & 0x7FFF);
+    }
+}
+
+/* binary32 -> binary16, round to nearest, ties to even, subnormals kept,  */
+/* overflow to infinity (magnitudes >= 65520, the midpoint past 65504).    */
+uint16_t oracle_f32_to_f16(float x)
+{
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    double a;
+    int e;
+    double m;
+    if (isnan(x))
+        return sign | 0x7E00;
+    a = fabs((double)x);
+    if (a >= 65520.0)                /* includes infinity */
+        return sign | 0x7C00;
+    if (a < 0x1p-14)                 /* subnormal range, spacing 2^-24; 1024 is 0x0400 */
+        return sign | (uint16_t)rint(a * 0x1p24);
+    e = ilogb(a);                    /* -14 <= e <= 15 */
+    m = rint(ldexp(a, 10 - e));      /* 1024 .. 2048 */
+    if (m == 2048.0) {
+        m = 1024.0;
+        e += 1;
+    }
+    return sign | (uint16_t)(((e + 15) << 10) | ((int)m - 1024));
+}
+
+void oracle_f32_to_bf16_array(const float *x, uint16_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16(x[i]);
+}
+
+void oracle_f32_to_f16_array(const float *x, uint16_t *out, int64_t n)
+{
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_f16(x[i]);
+}
+
+#define ORACLE_OUT_BF16 0
+#define ORACLE_OUT_F16 1
+static uint16_t narrow(float x, int32_t out_dtype)
+{
+    return out_dtype == ORACLE_OUT_F16 ? oracle_f32_to_f16(x) : oracle_f32_to_bf16(x);
+}
+
+/* ------------------------------------------------------------------ */
+/* [P1] gather, followed by the dequantisation the stored scale stands  */
+/* for: value = E4M3 decode(code) * scale in binary32 (the product       */
+/* rounded once), then rounded to the output type (bf16 or fp16, to      */
+/* nearest even).  Row cu_seq_lens[r] + i of out [num_tokens, D] gets    */
+/* token i of request r, from page block_table[r][i / B], offset i % B.  */
+/* The same skip rules as the gather; other rows are left untouched.     */
+/* ------------------------------------------------------------------ */
+void oracle_gather_indexer_k_dequant(const uint8_t *kv_cache, uint16_t *out,
+                                     int64_t out_row_stride, int32_t out_dtype,
+                                     const int32_t *block_table, const int32_t *cu_seq_lens,
+                                     int32_t num_reqs, int32_t max_blocks_per_req,
+                                     int64_t num_tokens, int64_t num_blocks,
+                                     int64_t cache_block_stride, int32_t block_size,
+                                     int32_t head_dim)
+{
+    int32_t r;
+    for (r = 0; r < num_reqs; ++r) {
+        int64_t start = cu_seq_lens[r];
+        int64_t len = (int64_t)cu_seq_lens[r + 1] - start;
+        int64_t i;
+        for (i = 0; i < len; ++i) {
+            int64_t row = start + i;
+            int64_t j = i / block_size;
+            int64_t off = i % block_size;
+            int64_t page;
+            const uint8_t *base;
+            uint8_t le[4];
+            uint32_t sb;
+            float s;
+            int d;
+            if (row < 0 || row >= num_tokens)
+                continue;
+            if (j >= max_blocks_per_req)
+                continue;
+            page = block_table[(int64_t)r * max_blocks_per_req + j];
+            if (page < 0 || page >= num_blocks)
+                continue;
+            base = kv_cache + page * cache_block_stride;
+            memcpy(le, base + (int64_t)block_size * head_dim + off * 4, 4);
+            sb = (uint32_t)le[0] | ((uint32_t)le[1] << 8) | ((uint32_t)le[2] << 16) |
+                 ((uint32_t)le[3] << 24);
+            memcpy(&s, &sb, 4);
+            for (d = 0; d < head_dim; ++d) {
+                float v = oracle_e4m3_decode(base[off * head_dim + d]) * s;
+                out[row * out_row_stride + d] = narrow(v, out_dtype);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* [P3] NVFP4 pages read back: for each request r and token i, from page */
+/* block_table[r][i / B] at offset i % B, for K and V, every head h and  */
+/* 16-element group g: the block scale byte (K at (off, g), V at its     */
+/* swizzled position), sfd = E4M3 decode of it, and for element k the   */
+/* value E2M1 decode(code_k) * sfd (exact in binary32: at most 6         */
+/* significant bits) times the per-tensor scale (k_scale or v_scale, the */
+/* store's global scale is its reciprocal), rounded once in binary32 and */
+/* then to the output type.  Rows go to cu_seq_lens[r] + i of            */
+/* key_out / value_out [num_tokens, H, D] (row strides in elements).     */
+/* Same page layout, HND / NHD, and skip rules as the store and gather.  */
+/* ------------------------------------------------------------------ */
+void oracle_gather_kv_fp4_dequant(const uint8_t *key_cache, const uint8_t *value_cache,
+                                  uint16_t *key_out, int64_t key_row_stride,
+                                  uint16_t *value_out, int64_t value_row_stride,
+                                  int32_t out_dtype, const int32_t *block_table,
+                                  const int32_t *cu_seq_lens, int32_t num_reqs,
+                                  int32_t max_blocks_per_req, int64_t num_tokens,
+                                  int32_t num_heads, int32_t head_size, int32_t block_size,
+                                  int64_t num_blocks, int64_t page_stride, int32_t layout,
+                                  float k_scale, float v_scale)
+{
+    const int64_t data_dim = head_size / 2;
+    const int64_t S = head_size / 16;
+    const int64_t data_per_side = (int64_t)num_heads * block_size * data_dim;
+    int32_t r;
+    for (r = 0; r < num_reqs; ++r) {
+        int64_t start = cu_seq_lens[r];
+        int64_t len = (int64_t)cu_seq_lens[r + 1] - start;
+        int64_t i;
+        for (i = 0; i < len; ++i) {
+            int64_t row = start + i;
+            int64_t j = i / block_size;
+            int64_t off = i % block_size;
+            int64_t page;
+            int kv;
+            if (row < 0 || row >= num_tokens)
+                continue;
+            if (j >= max_blocks_per_req)
+                continue;
+            page = block_table[(int64_t)r * max_blocks_per_req + j];
+            if (page < 0 || page >= num_blocks)
+                continue;
+            for (kv = 0; kv < 2; ++kv) {
+                const uint8_t *side = ((kv == 0) ? key_cache : value_cache) + page * page_stride;
+                const uint8_t *scales = side + data_per_side;
+                uint16_t *dst = (kv == 0) ? key_out + row * key_row_stride
+                                          : value_out + row * value_row_stride;
+                float ts = (kv == 0) ? k_scale : v_scale;
+                int32_t h;
+                int64_t g;
+                for (h = 0; h < num_heads; ++h) {
+                    for (g = 0; g < S; ++g) {
+                        int64_t data_off, scale_off, srow, scol;
+                        float sfd;
+                        int k2;
+                        if (layout == 0)
+                            data_off = ((int64_t)h * block_size + off) * data_dim + g * 8;
+                        else
+                            data_off = (off * num_heads + h) * data_dim + g * 8;
+                        if (kv == 0) {
+                            srow = off;
+                            scol = g;
+                        } else {
+                            int sw = oracle_swizzle_offset((int)off, (int)g, (int)S);
+                            srow = sw / S;
+                            scol = sw % S;
+                        }
+                        if (layout == 0)
+                            scale_off = ((int64_t)h * block_size + srow) * S + scol;
+                        else
+                            scale_off = (srow * num_heads + h) * S + scol;
+                        sfd = oracle_e4m3_decode(scales[scale_off]);
+                        for (k2 = 0; k2 < 16; ++k2) {
+                            uint8_t byte = side[data_off + k2 / 2];
+                            uint8_t code = (k2 % 2) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 0xF);
+                            float v = oracle_e2m1_decode(code) * sfd;
+                            v = v * ts;
+                            dst[(int64_t)h * head_size + g * 16 + k2] = narrow(v, out_dtype);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}

@@ -220,6 +220,10 @@ class Fp4Workload:
     v_scale: float
     cache_init: np.ndarray           # uint8 [num_blocks, 2, side_bytes]
     dtype: str = "bf16"              # source element type: "bf16" or "f16"
+    # when the slots come from request lengths: the pages each request owns
+    # and the token offsets of the requests (for reading the pages back)
+    block_table: np.ndarray = None   # int32 [R, maxb]
+    cu_seq_lens: np.ndarray = None   # int32 [R+1]
 
     @property
     def side_bytes(self) -> int:
@@ -233,10 +237,12 @@ class Fp4Workload:
 def _fp4(name, seed, T, H, D, B, num_blocks, layout=0, slots=None, drop_frac=0.05,
          lens=None, dtype="bf16"):
     g = rng(seed)
+    table = cu = None
     if lens is not None:
         table, _ = _pages_table(g, lens, B, num_blocks)
         slot_mapping = slots_from_table(table, lens, B)
         T = slot_mapping.shape[0]
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     elif slots is None:
         slot_mapping = g.permutation(num_blocks * B)[:T].astype(np.int64)
     else:
@@ -250,7 +256,8 @@ def _fp4(name, seed, T, H, D, B, num_blocks, layout=0, slots=None, drop_frac=0.0
     side = H * B * (D // 2 + D // 16)
     cache = random_bytes(g, (num_blocks, 2, side))
     return Fp4Workload(name, H, D, B, num_blocks, layout, half_bits(kf, dtype),
-                       half_bits(vf, dtype), slot_mapping, k_scale, v_scale, cache, dtype)
+                       half_bits(vf, dtype), slot_mapping, k_scale, v_scale, cache, dtype,
+                       table, cu)
 
 
 def c5_nvfp4_store(layout=0, dtype="bf16") -> Fp4Workload:
