@@ -25,6 +25,16 @@
  *                             reshape_and_cache_nvfp4_kernel and
  *                             reshape_and_cache_nvfp4_dispatch).
  *
+ * and, on the reader side, two gathers that return the cached keys (and
+ * values) dequantised to bf16 or fp16 rows for consumers without fp8 / fp4
+ * inputs:
+ *
+ *   pkv_gather_indexer_k_dequant  the gather above, each element then
+ *                             E4M3 decode(code) * scale.
+ *   pkv_gather_kv_fp4_dequant  NVFP4 pages back to K and V rows, each element
+ *                             E2M1 decode(code) * block scale * k_scale
+ *                             (v_scale for V).
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every buffer pointer is a DEVICE pointer owned by the caller.  The
@@ -65,12 +75,13 @@ extern "C" {
 #define PKV_LAYOUT_NHD 1       /* per page side: data [B][H][D/2], scales [B][H][D/16] */
 
 /* Source element types of the stores (the NVFP4 store's dispatcher on the
- * vLLM page covers both 16-bit float types); both widen exactly to binary32. */
+ * vLLM page covers both 16-bit float types); both widen exactly to binary32.
+ * The same two are the output types of the dequantising gathers. */
 #define PKV_DTYPE_BF16 0
 #define PKV_DTYPE_F16 1
 
 /* ABI version of this header; bumped when a signature changes. */
-#define PKV_ABI_VERSION 2
+#define PKV_ABI_VERSION 3
 int pkv_abi_version(void);
 
 /* Message for the last non-zero status on this thread ("" if none). */
@@ -177,6 +188,79 @@ int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
                      const float *k_scale, const float *v_scale, void *stream);
 
 /*
+ * Dequantising gather of the indexer K cache (the gather of vLLM PR "Add
+ * gather_indexer_k_quant_cache kernel" followed by the dequantisation its
+ * per-token scale stands for).
+ *
+ * For each request r and token i of it, with page, off and row as for
+ * pkv_gather_indexer_k_fp8 and s the binary32 scale of the token (page bytes
+ * [block_size*head_dim + off*4, +4), little-endian):
+ *     out[row*out_row_stride + d] = ROUND(binary32(E4M3 decode(code_d) * s))
+ * for d < head_dim, where ROUND is round to nearest even into bf16 or fp16
+ * (out_dtype; overflow gives infinity).  The same skip rules as the gather;
+ * no other output element is written.
+ *
+ *   kv_cache         as for the gather (16-byte aligned, stride a multiple
+ *                    of 16 and >= block_size*(head_dim+4)).
+ *   out              [num_tokens, >= head_dim] bf16 or fp16, row stride
+ *                    out_row_stride ELEMENTS (>= head_dim, multiple of 8);
+ *                    16-byte aligned; written.
+ *   out_dtype        PKV_DTYPE_BF16 or PKV_DTYPE_F16.
+ *   block_table, cu_seq_lens, sizes: as for the gather.
+ * Codes 0x7F / 0xFF (NaN) and non-finite scales are never written by the
+ * store; reading them gives NaN or infinity (NaN bits unspecified).
+ * Errors: as for the gather, plus PKV_EINVAL for a bad out_dtype or row
+ * stride and PKV_EALIGN for a row stride that is not a multiple of 8.
+ */
+int pkv_gather_indexer_k_dequant(const void *kv_cache, void *out, int64_t out_row_stride,
+                                 int32_t out_dtype, const int32_t *block_table,
+                                 const int32_t *cu_seq_lens, int32_t num_reqs,
+                                 int32_t max_blocks_per_req, int64_t num_tokens,
+                                 int64_t num_blocks, int64_t cache_block_stride,
+                                 int32_t block_size, int32_t head_dim, void *stream);
+
+/*
+ * NVFP4 K/V pages read back (the inverse of pkv_store_kv_fp4 up to its
+ * quantisation; page layout, HND / NHD and the V-scale swizzle as there).
+ *
+ * For each request r and token i of it: page = block_table[r *
+ * max_blocks_per_req + i / block_size], off = i % block_size, row =
+ * cu_seq_lens[r] + i; for K then V, every head h and 16-element group g:
+ * sfd = E4M3 decode of the group's scale byte, and for element k
+ *     out[row*row_stride + h*head_size + 16g + k] =
+ *         ROUND(binary32(E2M1 decode(code_k) * sfd * scale))
+ * where E2M1 decode(code_k) * sfd is exact, scale = *k_scale for K and
+ * *v_scale for V (the store's global scale is their reciprocal), and ROUND is
+ * round to nearest even into bf16 or fp16 (out_dtype).  Skip rules as for the
+ * gathers; no other output element is written.
+ *
+ *   key_cache,
+ *   value_cache      side 0 / side 1 of page 0, as for the store; 16-byte
+ *                    aligned; page_stride a multiple of 16 and >= the side
+ *                    size H*B*(D/2 + D/16).
+ *   key_out,
+ *   value_out        [num_tokens, >= H*D] bf16 or fp16, row strides in
+ *                    ELEMENTS (>= H*D, multiples of 8); 16-byte aligned;
+ *                    written.
+ *   block_table      int32 [num_reqs, max_blocks_per_req].
+ *   cu_seq_lens      int32 [num_reqs + 1].
+ *   k_scale,
+ *   v_scale          device binary32 scalars.
+ *   head_size        multiple of 64; block_size multiple of 4.
+ * NaN scale bytes (0x7F / 0xFF) are never written by the store; reading them
+ * gives NaN (bits unspecified).
+ */
+int pkv_gather_kv_fp4_dequant(const void *key_cache, const void *value_cache, void *key_out,
+                              int64_t key_row_stride, void *value_out,
+                              int64_t value_row_stride, int32_t out_dtype,
+                              const int32_t *block_table, const int32_t *cu_seq_lens,
+                              int32_t num_reqs, int32_t max_blocks_per_req,
+                              int64_t num_tokens, int32_t num_heads, int32_t head_size,
+                              int32_t block_size, int64_t num_blocks, int64_t page_stride,
+                              int32_t layout, const float *k_scale, const float *v_scale,
+                              void *stream);
+
+/*
  * Diagnostics: the device codecs the store kernels use, exposed so that a
  * test can sweep them over every binary32 input.
  *   pkv_diag_encode_e4m3: out[i] = E4M3(y[i]); defined for |y[i]| < 464
@@ -187,6 +271,14 @@ int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
  */
 int pkv_diag_encode_e4m3(const float *y, uint8_t *out, int64_t n, void *stream);
 int pkv_diag_encode_e2m1(const float *y, uint8_t *out, int64_t n, void *stream);
+
+/*
+ * Diagnostic: the output rounding of the dequantising gathers,
+ * out[i] = ROUND(x[i]) into bf16 or fp16 (out_dtype), round to nearest even.
+ * x: binary32 [n], 16-byte aligned; out: 16-bit [n], 16-byte aligned; n a
+ * multiple of 16.  NaN inputs give NaN (bits unspecified).
+ */
+int pkv_diag_narrow(const float *x, uint16_t *out, int64_t n, int32_t out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

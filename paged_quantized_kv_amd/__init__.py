@@ -18,6 +18,7 @@ import torch
 
 __all__ = [
     "pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
+    "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant", "pkv_diag_narrow",
     "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "PkvError", "LAYOUT_HND", "LAYOUT_NHD",
     "library_path", "abi_version",
 ]
@@ -71,10 +72,16 @@ def _load():
     lib.pkv_store_indexer_k_fp8.argtypes = [P, i64, i32, P, i64, P, i64, i64, i32, i32, P]
     lib.pkv_store_kv_fp4.argtypes = [P, i64, P, i64, i32, P, P, P, i64, i32, i32, i32, i64, i64,
                                      i32, P, P, P]
+    lib.pkv_gather_indexer_k_dequant.argtypes = [P, P, i64, i32, P, P, i32, i32, i64, i64,
+                                                 i64, i32, i32, P]
+    lib.pkv_gather_kv_fp4_dequant.argtypes = [P, P, P, i64, P, i64, i32, P, P, i32, i32, i64,
+                                              i32, i32, i32, i64, i64, i32, P, P, P]
     lib.pkv_diag_encode_e4m3.argtypes = [P, P, i64, P]
+    lib.pkv_diag_narrow.argtypes = [P, P, i64, i32, P]
     lib.pkv_diag_encode_e2m1.argtypes = [P, P, i64, P]
     for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
-                 "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1"):
+                 "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
+                 "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "pkv_diag_narrow"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -247,6 +254,96 @@ def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, 
         v_scale.data_ptr(), _stream(stream)))
 
 
+def _table_args(block_table, cu_seq_lens):
+    _dev(block_table, "block_table", torch.int32)
+    _dev(cu_seq_lens, "cu_seq_lens", torch.int32)
+    _contig(block_table, "block_table")
+    _contig(cu_seq_lens, "cu_seq_lens")
+    if block_table.dim() != 2 or cu_seq_lens.dim() != 1:
+        raise ValueError("block_table must be 2-D and cu_seq_lens 1-D")
+    num_reqs, max_blocks = block_table.shape
+    if cu_seq_lens.numel() != num_reqs + 1:
+        raise ValueError(f"cu_seq_lens must have num_reqs + 1 = {num_reqs + 1} entries")
+    return num_reqs, max_blocks
+
+
+def pkv_gather_indexer_k_dequant(kv_cache, out, block_table, cu_seq_lens,
+                                 block_size: int | None = None, stream=None):
+    """Gather the indexer keys of every request and dequantise them into out.
+
+    kv_cache:   uint8 indexer pages, as for pkv_gather_indexer_k_fp8.
+    out:        bfloat16 or float16 [num_tokens, head_dim] (row stride free), written:
+                out[row, d] = round(E4M3 decode(code) * scale).
+    block_table int32 [num_reqs, max_blocks_per_req], cu_seq_lens int32 [num_reqs + 1].
+    """
+    _dev(kv_cache, "kv_cache", torch.uint8)
+    _dev(out, "out")
+    out_dtype = _src_dtype(out, "out")
+    if out.dim() != 2 or out.stride(1) != 1:
+        raise ValueError("out must be [num_tokens, head_dim] with contiguous rows")
+    num_tokens, head_dim = out.shape
+    num_reqs, max_blocks = _table_args(block_table, cu_seq_lens)
+    if block_size is None:
+        if kv_cache.dim() != 3:
+            raise ValueError("pass block_size, or kv_cache as [num_blocks, block_size, D + 4]")
+        block_size = kv_cache.shape[1]
+    if kv_cache.dim() >= 2 and kv_cache.stride(-1) != 1:
+        raise ValueError("kv_cache pages must be contiguous")
+    _check(_lib.pkv_gather_indexer_k_dequant(
+        kv_cache.data_ptr(), out.data_ptr(), out.stride(0), out_dtype, block_table.data_ptr(),
+        cu_seq_lens.data_ptr(), num_reqs, max_blocks, num_tokens, kv_cache.shape[0],
+        kv_cache.stride(0), block_size, head_dim, _stream(stream)))
+
+
+def pkv_gather_kv_fp4_dequant(key_cache, value_cache, key_out, value_out, block_table,
+                              cu_seq_lens, k_scale, v_scale, block_size: int | None = None,
+                              layout: int | None = None, stream=None):
+    """Read NVFP4 K/V pages back into bfloat16 or float16 rows.
+
+    key_cache / value_cache: uint8 views of the two page sides, as for
+    pkv_store_kv_fp4 (a 4-D [num_blocks, block_size, num_heads, D/2 + D/16]
+    view supplies block_size and the layout).  key_out / value_out: bf16 or
+    fp16 [num_tokens, num_heads, head_size] (only stride(0) free), written:
+    element = round(E2M1 decode(code) * block scale * k_scale (v_scale)).
+    """
+    _dev(key_out, "key_out")
+    _dev(value_out, "value_out")
+    out_dtype = _src_dtype(key_out, "key_out")
+    if value_out.dtype != key_out.dtype:
+        raise TypeError("key_out and value_out must have the same dtype")
+    _dev(key_cache, "key_cache", torch.uint8)
+    _dev(value_cache, "value_cache", torch.uint8)
+    _dev(k_scale, "k_scale", torch.float32)
+    _dev(v_scale, "v_scale", torch.float32)
+    if key_out.dim() != 3 or value_out.shape != key_out.shape:
+        raise ValueError("key_out and value_out must both be [num_tokens, num_heads, head_size]")
+    num_tokens, num_heads, head_size = key_out.shape
+    for t, n in ((key_out, "key_out"), (value_out, "value_out")):
+        if t.stride(2) != 1 or t.stride(1) != head_size:
+            raise ValueError(f"{n}: heads and elements must be contiguous (only stride(0) is free)")
+    if k_scale.numel() != 1 or v_scale.numel() != 1:
+        raise ValueError("k_scale and v_scale must be scalars")
+    num_reqs, max_blocks = _table_args(block_table, cu_seq_lens)
+    if key_cache.dim() == 4:
+        full_dim = head_size // 2 + head_size // 16
+        if key_cache.shape[3] != full_dim or key_cache.shape[2] != num_heads:
+            raise ValueError(f"key_cache must be [num_blocks, block_size, {num_heads}, {full_dim}]")
+        if block_size is None:
+            block_size = key_cache.shape[1]
+        if layout is None:
+            layout = LAYOUT_HND if key_cache.stride(2) > key_cache.stride(1) else LAYOUT_NHD
+    elif block_size is None or layout is None:
+        raise ValueError("pass block_size and layout, or 4-D cache views")
+    if key_cache.stride(0) != value_cache.stride(0) or key_cache.shape[0] != value_cache.shape[0]:
+        raise ValueError("key_cache and value_cache must share num_blocks and page stride")
+    _check(_lib.pkv_gather_kv_fp4_dequant(
+        key_cache.data_ptr(), value_cache.data_ptr(), key_out.data_ptr(), key_out.stride(0),
+        value_out.data_ptr(), value_out.stride(0), out_dtype, block_table.data_ptr(),
+        cu_seq_lens.data_ptr(), num_reqs, max_blocks, num_tokens, num_heads, head_size,
+        block_size, key_cache.shape[0], key_cache.stride(0), layout, k_scale.data_ptr(),
+        v_scale.data_ptr(), _stream(stream)))
+
+
 def pkv_diag_encode_e4m3(y, out, stream=None):
     """out[i] = device E4M3 code of y[i] (defined for |y| < 464)."""
     _contig(_dev(y, "y", torch.float32), "y")
@@ -263,3 +360,13 @@ def pkv_diag_encode_e2m1(y, out, stream=None):
     if out.numel() != y.numel():
         raise ValueError("out must have y.numel() bytes")
     _check(_lib.pkv_diag_encode_e2m1(y.data_ptr(), out.data_ptr(), y.numel(), _stream(stream)))
+
+
+def pkv_diag_narrow(x, out, stream=None):
+    """out[i] = device bf16 / fp16 rounding of x[i] (the dequantising gathers' output step)."""
+    _contig(_dev(x, "x", torch.float32), "x")
+    _contig(_dev(out, "out"), "out")
+    dt = _src_dtype(out, "out")
+    if out.numel() != x.numel():
+        raise ValueError("out must have x.numel() elements")
+    _check(_lib.pkv_diag_narrow(x.data_ptr(), out.data_ptr(), x.numel(), dt, _stream(stream)))

@@ -25,6 +25,7 @@ SOURCES = [
     "gather_indexer_k_fp8.hip",
     "store_indexer_k_fp8.hip",
     "store_kv_fp4.hip",
+    "gather_dequant.hip",
     "diag_codecs.hip",
 ]
 

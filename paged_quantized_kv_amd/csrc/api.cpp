@@ -177,6 +177,98 @@ int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,
   return launched(pkv::launch_store_kv_fp4(a, static_cast<hipStream_t>(stream)), op);
 }
 
+int pkv_gather_indexer_k_dequant(const void* kv_cache, void* out, int64_t out_row_stride,
+                                 int32_t out_dtype, const int32_t* block_table,
+                                 const int32_t* cu_seq_lens, int32_t num_reqs,
+                                 int32_t max_blocks_per_req, int64_t num_tokens,
+                                 int64_t num_blocks, int64_t cache_block_stride,
+                                 int32_t block_size, int32_t head_dim, void* stream) {
+  static const char* op = "pkv_gather_indexer_k_dequant";
+  if (num_reqs < 0) return fail(PKV_EINVAL, "%s: num_reqs must be >= 0, got %d", op, num_reqs);
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens must be >= 0, got %lld", op, (long long)num_tokens);
+  if (int rc = check_indexer_geometry(op, num_blocks, cache_block_stride, block_size, head_dim)) return rc;
+  if (max_blocks_per_req < 0)
+    return fail(PKV_EINVAL, "%s: max_blocks_per_req must be >= 0, got %d", op, max_blocks_per_req);
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F16)
+    return fail(PKV_EINVAL, "%s: out_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, out_dtype);
+  if (out_row_stride < head_dim)
+    return fail(PKV_EINVAL, "%s: out_row_stride %lld is smaller than head_dim %d", op, (long long)out_row_stride, head_dim);
+  if (out_row_stride % 8 != 0)
+    return fail(PKV_EALIGN, "%s: out_row_stride must be a multiple of 8 elements", op);
+  if (num_reqs == 0 || num_tokens == 0 || max_blocks_per_req == 0) return ok();
+  if ((int64_t)num_reqs * max_blocks_per_req > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req exceeds 2^31-1", op);
+  if (!kv_cache || !out || !block_table || !cu_seq_lens)
+    return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(kv_cache, 16) || !aligned(out, 16))
+    return fail(PKV_EALIGN, "%s: kv_cache and out must be 16-byte aligned", op);
+  if (!aligned(block_table, 4) || !aligned(cu_seq_lens, 4))
+    return fail(PKV_EALIGN, "%s: block_table and cu_seq_lens must be 4-byte aligned", op);
+  pkv::GatherDequantArgs a{static_cast<const uint8_t*>(kv_cache), static_cast<uint16_t*>(out),
+                           out_row_stride, out_dtype, block_table, cu_seq_lens, num_reqs,
+                           max_blocks_per_req, num_tokens, num_blocks, cache_block_stride,
+                           block_size, head_dim};
+  return launched(pkv::launch_gather_indexer_k_dequant(a, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_gather_kv_fp4_dequant(const void* key_cache, const void* value_cache, void* key_out,
+                              int64_t key_row_stride, void* value_out, int64_t value_row_stride,
+                              int32_t out_dtype, const int32_t* block_table,
+                              const int32_t* cu_seq_lens, int32_t num_reqs,
+                              int32_t max_blocks_per_req, int64_t num_tokens, int32_t num_heads,
+                              int32_t head_size, int32_t block_size, int64_t num_blocks,
+                              int64_t page_stride, int32_t layout, const float* k_scale,
+                              const float* v_scale, void* stream) {
+  static const char* op = "pkv_gather_kv_fp4_dequant";
+  if (num_reqs < 0) return fail(PKV_EINVAL, "%s: num_reqs must be >= 0, got %d", op, num_reqs);
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens must be >= 0, got %lld", op, (long long)num_tokens);
+  if (max_blocks_per_req < 0)
+    return fail(PKV_EINVAL, "%s: max_blocks_per_req must be >= 0, got %d", op, max_blocks_per_req);
+  if (num_heads <= 0) return fail(PKV_EINVAL, "%s: num_heads must be > 0, got %d", op, num_heads);
+  if (head_size <= 0) return fail(PKV_EINVAL, "%s: head_size must be > 0, got %d", op, head_size);
+  if (block_size <= 0) return fail(PKV_EINVAL, "%s: block_size must be > 0, got %d", op, block_size);
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "%s: num_blocks must be > 0, got %lld", op, (long long)num_blocks);
+  if (head_size % 64 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: head_size must be a multiple of 64, got %d", op, head_size);
+  if (block_size % 4 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size must be divisible by 4, got %d", op, block_size);
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F16)
+    return fail(PKV_EINVAL, "%s: out_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, out_dtype);
+  if (layout != PKV_LAYOUT_HND && layout != PKV_LAYOUT_NHD)
+    return fail(PKV_EINVAL, "%s: layout must be PKV_LAYOUT_HND or PKV_LAYOUT_NHD, got %d", op, layout);
+  const int64_t hd = (int64_t)num_heads * head_size;
+  if (hd > ((int64_t)1 << 24)) return fail(PKV_EUNSUPPORTED, "%s: num_heads*head_size too large", op);
+  if (key_row_stride < hd || value_row_stride < hd)
+    return fail(PKV_EINVAL, "%s: row strides must be >= num_heads*head_size = %lld", op, (long long)hd);
+  if (key_row_stride % 8 != 0 || value_row_stride % 8 != 0)
+    return fail(PKV_EALIGN, "%s: row strides must be multiples of 8 elements", op);
+  const int64_t side = (int64_t)num_heads * block_size * (head_size / 2 + head_size / 16);
+  if (page_stride < side)
+    return fail(PKV_EUNSUPPORTED, "%s: page_stride %lld is smaller than one side, %lld bytes", op,
+                (long long)page_stride, (long long)side);
+  if (page_stride % 16 != 0) return fail(PKV_EALIGN, "%s: page_stride must be a multiple of 16", op);
+  if (num_reqs == 0 || num_tokens == 0 || max_blocks_per_req == 0) return ok();
+  if ((int64_t)num_reqs * max_blocks_per_req * 2 * num_heads > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req * 2 * num_heads exceeds 2^31-1", op);
+  if (!key_cache || !value_cache || !key_out || !value_out || !block_table || !cu_seq_lens ||
+      !k_scale || !v_scale)
+    return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(key_cache, 16) || !aligned(value_cache, 16) || !aligned(key_out, 16) ||
+      !aligned(value_out, 16))
+    return fail(PKV_EALIGN, "%s: caches and outputs must be 16-byte aligned", op);
+  if (!aligned(block_table, 4) || !aligned(cu_seq_lens, 4) || !aligned(k_scale, 4) ||
+      !aligned(v_scale, 4))
+    return fail(PKV_EALIGN, "%s: block_table, cu_seq_lens and the scales must be 4-byte aligned", op);
+  pkv::GatherFp4DequantArgs a{static_cast<const uint8_t*>(key_cache),
+                              static_cast<const uint8_t*>(value_cache),
+                              static_cast<uint16_t*>(key_out), key_row_stride,
+                              static_cast<uint16_t*>(value_out), value_row_stride, out_dtype,
+                              block_table, cu_seq_lens, num_reqs, max_blocks_per_req, num_tokens,
+                              num_heads, head_size, block_size, num_blocks, page_stride, layout,
+                              k_scale, v_scale};
+  return launched(pkv::launch_gather_kv_fp4_dequant(a, static_cast<hipStream_t>(stream)), op);
+}
+
 static int check_diag(const char* op, const float* y, const uint8_t* out, int64_t n) {
   if (n < 0 || n % 16 != 0) return fail(PKV_EINVAL, "%s: n must be a non-negative multiple of 16", op);
   if (n > 0 && (!y || !out)) return fail(PKV_EINVAL, "%s: null buffer pointer", op);
@@ -196,6 +288,15 @@ int pkv_diag_encode_e2m1(const float* y, uint8_t* out, int64_t n, void* stream) 
   if (int rc = check_diag(op, y, out, n)) return rc;
   if (n == 0) return ok();
   return launched(pkv::launch_diag_e2m1(y, out, n, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_diag_narrow(const float* x, uint16_t* out, int64_t n, int32_t out_dtype, void* stream) {
+  static const char* op = "pkv_diag_narrow";
+  if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F16)
+    return fail(PKV_EINVAL, "%s: out_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, out_dtype);
+  if (int rc = check_diag(op, x, reinterpret_cast<const uint8_t*>(out), n)) return rc;
+  if (n == 0) return ok();
+  return launched(pkv::launch_diag_narrow(x, out, n, out_dtype, static_cast<hipStream_t>(stream)), op);
 }
 
 }  // extern "C"

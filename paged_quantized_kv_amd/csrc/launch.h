@@ -69,10 +69,53 @@ struct StoreFp4Args {
   const float* v_scale;
 };
 
+struct GatherDequantArgs {
+  const uint8_t* kv_cache;
+  uint16_t* out;
+  int64_t out_row_stride;
+  int32_t out_dtype;  // PKV_DTYPE_BF16 / PKV_DTYPE_F16
+  const int32_t* block_table;
+  const int32_t* cu_seq_lens;
+  int32_t num_reqs;
+  int32_t max_blocks_per_req;
+  int64_t num_tokens;
+  int64_t num_blocks;
+  int64_t cache_block_stride;
+  int32_t block_size;
+  int32_t head_dim;
+};
+
+struct GatherFp4DequantArgs {
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  uint16_t* key_out;
+  int64_t key_row_stride;
+  uint16_t* value_out;
+  int64_t value_row_stride;
+  int32_t out_dtype;
+  const int32_t* block_table;
+  const int32_t* cu_seq_lens;
+  int32_t num_reqs;
+  int32_t max_blocks_per_req;
+  int64_t num_tokens;
+  int32_t num_heads;
+  int32_t head_size;
+  int32_t block_size;
+  int64_t num_blocks;
+  int64_t page_stride;
+  int32_t layout;
+  const float* k_scale;
+  const float* v_scale;
+};
+
 int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream);
+int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stream);
+int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream);
 int launch_store_indexer_k_fp8(const StoreFp8Args& a, hipStream_t stream);
 int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream);
 int launch_diag_e4m3(const float* y, uint8_t* out, int64_t n, hipStream_t stream);
 int launch_diag_e2m1(const float* y, uint8_t* out, int64_t n, hipStream_t stream);
+int launch_diag_narrow(const float* x, uint16_t* out, int64_t n, int32_t out_dtype,
+                       hipStream_t stream);
 
 }  // namespace pkv

@@ -81,6 +81,9 @@ constexpr int kFp4Items = PKV_FP4_ITEMS;  // items per wave whose loads are in f
 #ifndef PKV_FP4_NT_SCALE
 #define PKV_FP4_NT_SCALE 0
 #endif
+#ifndef PKV_FP4_ORDER
+#define PKV_FP4_ORDER 0
+#endif
 #ifndef PKV_FP4_WPE
 #define PKV_FP4_WPE 0
 #endif
@@ -247,8 +250,13 @@ void store_kv_fp4_tile_kernel(
       valid[u] = item < num_items;  // wave-uniform
       const int64_t tile = item / sides_heads;
       const int32_t sh = (int32_t)(item - tile * sides_heads);
+#if PKV_FP4_ORDER
+      kv[u] = sh & 1;
+      h[u] = sh >> 1;
+#else
       kv[u] = sh >= num_heads;
       h[u] = kv[u] ? sh - num_heads : sh;
+#endif
       t0[u] = tile * kFp4Tile;
       // slot of token t0 + (lane % 16); tokens past the end have slot -1
       const int64_t my_t = t0[u] + (lane & (kFp4Tile - 1));

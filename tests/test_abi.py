@@ -25,6 +25,7 @@ def declared_symbols():
 def test_header_declares_the_boundary():
     syms = declared_symbols()
     for s in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
+              "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
               "pkv_last_error", "pkv_abi_version"):
         assert s in syms
 
@@ -37,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     for s in declared_symbols():
         assert s in exported, s
         assert getattr(lib, s) is not None
-    assert pkv.abi_version() == 2
+    assert pkv.abi_version() == 3
 
 
 def lib():
@@ -140,6 +141,70 @@ def test_store_fp4_validation(kw, code, msg):
 
 def test_store_fp4_empty_is_ok():
     assert store4(T=0, key=0, val=0, kc=0, vc=0, slots=0, kscale=0, vscale=0) == PKV_OK
+
+
+def gdq(**kw):
+    a = dict(kv_cache=A, out=A, ost=128, dt=0, block_table=A, cu=A, R=2, maxb=4, T=57, nb=8,
+             stride=64 * 132, B=64, D=128)
+    a.update(kw)
+    return lib().pkv_gather_indexer_k_dequant(a["kv_cache"], a["out"], a["ost"], a["dt"],
+                                              a["block_table"], a["cu"], a["R"], a["maxb"],
+                                              a["T"], a["nb"], a["stride"], a["B"], a["D"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=100, ost=104), PKV_EUNSUPPORTED, "multiple of 16"),
+    (dict(stride=64 * 132 + 8), PKV_EALIGN, "multiple of 16"),
+    (dict(dt=2), PKV_EINVAL, "out_dtype"),
+    (dict(ost=120), PKV_EINVAL, "out_row_stride"),
+    (dict(ost=132), PKV_EALIGN, "multiple of 8"),
+    (dict(out=0), PKV_EINVAL, "null"),
+    (dict(out=A + 8), PKV_EALIGN, "16-byte"),
+    (dict(R=-1), PKV_EINVAL, "num_reqs"),
+    (dict(R=70000, maxb=40000), PKV_EUNSUPPORTED, "2^31"),
+])
+def test_gather_dequant_validation(kw, code, msg):
+    assert gdq(**kw) == code
+    assert msg in last_error()
+
+
+def test_gather_dequant_empty_is_ok():
+    assert gdq(R=0, kv_cache=0, out=0, block_table=0, cu=0) == PKV_OK
+    assert gdq(T=0, kv_cache=0, out=0, block_table=0, cu=0) == PKV_OK
+
+
+def g4(**kw):
+    a = dict(kc=A, vc=A + 9216, ko=A, kst=1024, vo=A, vst=1024, dt=0, block_table=A, cu=A,
+             R=2, maxb=4, T=57, H=8, D=128, B=16, nb=8, page=18432, layout=0, kscale=A,
+             vscale=A)
+    a.update(kw)
+    return lib().pkv_gather_kv_fp4_dequant(a["kc"], a["vc"], a["ko"], a["kst"], a["vo"],
+                                           a["vst"], a["dt"], a["block_table"], a["cu"], a["R"],
+                                           a["maxb"], a["T"], a["H"], a["D"], a["B"], a["nb"],
+                                           a["page"], a["layout"], a["kscale"], a["vscale"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=96, kst=768, vst=768), PKV_EUNSUPPORTED, "multiple of 64"),
+    (dict(B=6), PKV_EUNSUPPORTED, "divisible by 4"),
+    (dict(layout=2), PKV_EINVAL, "layout"),
+    (dict(dt=5), PKV_EINVAL, "out_dtype"),
+    (dict(kst=1000), PKV_EINVAL, "row strides"),
+    (dict(vst=1028), PKV_EALIGN, "multiples of 8"),
+    (dict(page=9000), PKV_EUNSUPPORTED, "smaller than one side"),
+    (dict(page=18440), PKV_EALIGN, "page_stride"),
+    (dict(vc=A + 8), PKV_EALIGN, "16-byte"),
+    (dict(vscale=0), PKV_EINVAL, "null"),
+    (dict(H=0), PKV_EINVAL, "num_heads"),
+    (dict(maxb=-2), PKV_EINVAL, "max_blocks_per_req"),
+])
+def test_gather_fp4_dequant_validation(kw, code, msg):
+    assert g4(**kw) == code
+    assert msg in last_error()
+
+
+def test_gather_fp4_dequant_empty_is_ok():
+    assert g4(T=0, kc=0, vc=0, ko=0, vo=0, block_table=0, cu=0, kscale=0, vscale=0) == PKV_OK
 
 
 def test_diag_validation():
