@@ -21,6 +21,11 @@ store wrote at step i - 4, so no kernel reads data that the 256 MB Infinity
 Cache still holds from a recent write; the NVFP4 store reads 1 GB of K/V and
 writes 0.3 GB of pages per step.
 
+After the timed steps, the reader side is timed on the same batch (not part
+of `value`): pkv_gather_indexer_k_dequant (indexer pages -> bf16 rows) and
+pkv_gather_kv_fp4_dequant (NVFP4 pages -> bf16 K and V rows), reported under
+`reader_side`.
+
 Printed: one JSON line.  `value` = algorithmic bytes of one step / measured
 step time (GB/s); per-kernel durations come from HIP events recorded on the
 launch stream around each launch (timing-only events, without the cache
@@ -50,6 +55,8 @@ KERNEL_SOURCES = {
     "store_indexer_k_fp8": ["store_indexer_k_fp8.hip", "device_common.h"],
     "store_kv_fp4": ["store_kv_fp4.hip", "device_common.h"],
     "gather_indexer_k_fp8": ["gather_indexer_k_fp8.hip", "device_common.h"],
+    "gather_indexer_k_dequant": ["gather_dequant.hip", "device_common.h"],
+    "gather_kv_fp4_dequant": ["gather_dequant.hip", "device_common.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -84,6 +91,8 @@ def parse_args():
     p.add_argument("--sets", type=int, default=8, help="rotating indexer buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
+    p.add_argument("--reader-steps", type=int, default=50,
+                   help="timed iterations of the reader-side gathers (0: skip them)")
     p.add_argument("--calibration-copy", action="store_true",
                    help="run a plain 256 MiB fp32 copy-like kernel (torch.neg) before the "
                         "timed steps, for scaling hardware byte counters")
@@ -155,6 +164,13 @@ def algorithmic_bytes(T, D, H4, D4, R, maxb):
     return {"store_indexer_k_fp8": store8, "store_kv_fp4": fp4, "gather_indexer_k_fp8": gather}
 
 
+def reader_bytes(T, D, H4, D4, R, maxb, R4, maxb4):
+    """Bytes the reader-side gathers must move (read + write) over the batch."""
+    idx = T * (D + 4 + 2 * D) + R * maxb * 4 + (R + 1) * 4      # codes + scale -> bf16 row
+    fp4 = T * 2 * H4 * (D4 // 2 + D4 // 16 + 2 * D4) + R4 * maxb4 * 4 + (R4 + 1) * 4 + 8
+    return {"gather_indexer_k_dequant": idx, "gather_kv_fp4_dequant": fp4}
+
+
 def cpu_baseline(w, f, step_bytes):
     import numpy as np
 
@@ -175,6 +191,45 @@ def cpu_baseline(w, f, step_bytes):
             "mtokens_per_s": round(w.num_tokens / dt / 1e6, 4),
             "sample": "one full step (256 req x 1000 tok through fp8 store, NVFP4 store and "
                       "gather), plain C oracle, one thread"}
+
+
+def time_reader(args, pkv, torch, timing, stream, sets, w, f, bt, cu, c4, k4s, v4s):
+    """Average durations (ms) of the two reader-side gathers over the batch,
+    timed like the step's kernels.  The indexer read-back cycles over the
+    rotating page sets; the NVFP4 read-back reads the pages the last step
+    stored (0.3 GB, larger than the Infinity Cache)."""
+    T = w.num_tokens
+    H4, D4 = f.num_heads, f.head_size
+    outs = [torch.empty((T, w.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ko = torch.empty((T, H4, D4), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty((T, H4, D4), dtype=torch.bfloat16, device="cuda")
+    bt4, cu4 = (torch.from_numpy(a).to("cuda") for a in (f.block_table, f.cu_seq_lens))
+    names = ["gather_indexer_k_dequant", "gather_kv_fp4_dequant"]
+
+    def it(i, ev=None):
+        s = sets[i % len(sets)]
+        if ev is not None:
+            timing.record(ev[0], stream)
+        pkv.pkv_gather_indexer_k_dequant(s["cache"], outs[i % 2], bt, cu, block_size=w.block_size)
+        if ev is not None:
+            timing.record(ev[1], stream)
+        pkv.pkv_gather_kv_fp4_dequant(c4[:, 0], c4[:, 1], ko, vo, bt4, cu4, k4s, v4s,
+                                      block_size=f.block_size, layout=f.layout)
+        if ev is not None:
+            timing.record(ev[2], stream)
+
+    evs = [[timing.create() for _ in range(3)] for _ in range(args.reader_steps)]
+    for i in range(min(args.warmup, 20)):
+        it(i)
+    torch.cuda.synchronize()
+    for i in range(args.reader_steps):
+        it(i, evs[i])
+    torch.cuda.synchronize()
+    ms = {n: sum(timing.elapsed_ms(e[j], e[j + 1]) for e in evs) / args.reader_steps
+          for j, n in enumerate(names)}
+    del outs, ko, vo
+    timing.destroy_all()
+    return ms
 
 
 def main():
@@ -280,6 +335,18 @@ def main():
     timing.destroy_all()
     ms_per_step = wall * 1e3 / args.steps
 
+    reader = None
+    if args.reader_steps > 0:
+        reader = time_reader(args, pkv, torch, timing, stream, sets, w, f, bt, cu, c4, k4s, v4s)
+        R4, maxb4 = f.block_table.shape
+        rb = reader_bytes(T, D, H4, D4, R, maxb, R4, maxb4)
+        reader = {n: {"us": round(reader[n] * 1e3, 2), "alg_bytes": rb[n],
+                      "GBps": round(rb[n] / (reader[n] * 1e-3) / 1e9, 1),
+                      "frac_hbm_peak": round(rb[n] / (reader[n] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "mtokens_per_s": round(T / (reader[n] * 1e-3) / 1e6, 1),
+                      "traffic": measured_traffic(n)}
+                  for n in rb}
+
     alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
     step_bytes = sum(alg.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -324,6 +391,8 @@ def main():
         "roofline": roofline,
         "input_gen_s": round(t_gen, 1),
     }
+    if reader is not None:
+        out["reader_side"] = reader
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, f, step_bytes)
     print(json.dumps(out), flush=True)

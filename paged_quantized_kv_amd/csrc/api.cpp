@@ -195,6 +195,8 @@ int pkv_gather_indexer_k_dequant(const void* kv_cache, void* out, int64_t out_ro
     return fail(PKV_EINVAL, "%s: out_row_stride %lld is smaller than head_dim %d", op, (long long)out_row_stride, head_dim);
   if (out_row_stride % 8 != 0)
     return fail(PKV_EALIGN, "%s: out_row_stride must be a multiple of 8 elements", op);
+  if ((int64_t)block_size * head_dim / 8 > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size * head_dim / 8 exceeds 2^31-1", op);
   if (num_reqs == 0 || num_tokens == 0 || max_blocks_per_req == 0) return ok();
   if ((int64_t)num_reqs * max_blocks_per_req > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req exceeds 2^31-1", op);
@@ -247,9 +249,11 @@ int pkv_gather_kv_fp4_dequant(const void* key_cache, const void* value_cache, vo
     return fail(PKV_EUNSUPPORTED, "%s: page_stride %lld is smaller than one side, %lld bytes", op,
                 (long long)page_stride, (long long)side);
   if (page_stride % 16 != 0) return fail(PKV_EALIGN, "%s: page_stride must be a multiple of 16", op);
+  if ((int64_t)block_size * hd / 8 > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size * num_heads * head_size / 8 exceeds 2^31-1", op);
   if (num_reqs == 0 || num_tokens == 0 || max_blocks_per_req == 0) return ok();
-  if ((int64_t)num_reqs * max_blocks_per_req * 2 * num_heads > INT32_MAX)
-    return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req * 2 * num_heads exceeds 2^31-1", op);
+  if ((int64_t)num_reqs * max_blocks_per_req * 2 > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req * 2 exceeds 2^31-1", op);
   if (!key_cache || !value_cache || !key_out || !value_out || !block_table || !cu_seq_lens ||
       !k_scale || !v_scale)
     return fail(PKV_EINVAL, "%s: null buffer pointer", op);

@@ -159,6 +159,30 @@ __device__ __forceinline__ uint32_t xcd_contiguous_block() {
   return (b % kNumXcd) * (gridDim.x / kNumXcd) + b / kNumXcd;
 }
 
+// Division of n in [0, 2^31) by a divisor d in [1, 2^31) fixed for a launch,
+// without a divide instruction: q = (n * m) >> (31 + l) with l = ceil(log2 d)
+// and m = ceil(2^(31+l) / d).  Exact for every such n because
+// 0 <= m*d - 2^(31+l) < d <= 2^l (T. Granlund and P. L. Montgomery,
+// "Division by invariant integers using multiplication", PLDI 1994,
+// Theorem 4.2 with N = 31).  m < 2^32 and n*m < 2^63.
+struct FastDiv {
+  uint32_t d;
+  uint32_t m;
+  uint32_t shift;  // 31 + l
+  __host__ __device__ static FastDiv make(uint32_t divisor) {
+    FastDiv f;
+    f.d = divisor;
+    uint32_t l = 0;
+    while ((1ull << l) < divisor) ++l;
+    f.shift = 31 + l;
+    f.m = (uint32_t)(((1ull << (31 + l)) + divisor - 1) / divisor);
+    return f;
+  }
+  __device__ __forceinline__ uint32_t div(uint32_t n) const {
+    return (uint32_t)(((uint64_t)n * m) >> shift);
+  }
+};
+
 // slot -> (page, offset) for a block size that may or may not be a power of two.
 __device__ __forceinline__ void split_slot(int64_t slot, int32_t block_size, int32_t log2_bs,
                                            int64_t& page, int64_t& off) {

@@ -13,12 +13,13 @@
 // each element E2M1 decode(code) * E4M3 decode(block scale), which is exact,
 // times k_scale (v_scale for V) in binary32, then rounded to the output type.
 //
-// Both walk the block table directly: one wave per (table entry, ...) unit,
-// exiting at once when the entry holds no tokens of its request, with a
-// grid-stride loop so the grid never decides coverage.  A wave's loads
-// (16-byte code chunks, contiguous over the wave) are all issued before it
-// converts any of them; every 16-byte chunk of codes becomes 32 (fp8) or 64
-// (fp4) bytes of output, stored 16 bytes per lane.
+// Both walk the block table directly: one wave per table entry (and side,
+// for NVFP4), exiting at once when the entry holds no tokens of its request,
+// with a grid-stride loop so the grid never decides coverage.  A lane's unit
+// is 8 elements of output: 8 fp8 codes (8 bytes) or one half-block of fp4
+// codes (4 bytes) become one 16-byte store; units run in output order, so
+// every wave store covers 1 KB of contiguous rows.  A wave issues the loads
+// of several units before it converts any of them.
 //
 // Conversions are the gfx950 ones: v_cvt_pk_f32_fp8 (exact E4M3 decode),
 // v_cvt_scalef32_pk_f32_fp4 with unit scale (exact E2M1 decode),
@@ -35,7 +36,14 @@ namespace {
 
 constexpr int kDqThreads = 256;
 constexpr int kDqWaves = kDqThreads / kWave;
-constexpr int kDqUnroll = 4;  // 16-byte code chunks per lane in flight
+#ifndef PKV_IDX_DQ_UNROLL
+#define PKV_IDX_DQ_UNROLL 4
+#endif
+#ifndef PKV_FP4_DQ_UNROLL
+#define PKV_FP4_DQ_UNROLL 32
+#endif
+constexpr int kIdxUnroll = PKV_IDX_DQ_UNROLL;  // lane units (8 elements each) in flight, indexer
+constexpr int kFp4Unroll = PKV_FP4_DQ_UNROLL;  // lane units in flight, NVFP4
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -50,22 +58,6 @@ __device__ __forceinline__ uint32_t narrow2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   else
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// 16 E4M3 codes times s -> 16 narrowed outputs (32 bytes, element order).
-template <bool kF16>
-__device__ __forceinline__ void dequant16_fp8(const u32x4 codes, float s, u32x4& lo, u32x4& hi) {
-  uint32_t w[8];
-  const uint32_t c[4] = {codes.x, codes.y, codes.z, codes.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[q], false);  // bytes 0, 1
-    const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c[q], true);   // bytes 2, 3
-    w[2 * q] = narrow2<kF16>(a.x * s, a.y * s);
-    w[2 * q + 1] = narrow2<kF16>(b.x * s, b.y * s);
-  }
-  lo = u32x4{w[0], w[1], w[2], w[3]};
-  hi = u32x4{w[4], w[5], w[6], w[7]};
 }
 
 // The two E2M1 codes of byte kByte of `word` (low nibble first) times the
@@ -112,16 +104,19 @@ __device__ __forceinline__ bool table_entry_run(const int32_t* __restrict__ bloc
 }
 
 // ------------------------------------------------------------- indexer K
+// Work of a wave: one table entry's run of tokens.  Lane unit = 8 codes of
+// one token (an 8-byte load) -> 8 outputs (one 16-byte store), so every wave
+// load covers 512 contiguous code bytes and every wave store 1 KB of rows.
 template <bool kF16>
 __global__ __launch_bounds__(kDqThreads) void gather_indexer_k_dequant_kernel(
     const uint8_t* __restrict__ kv_cache, uint16_t* __restrict__ out, int64_t out_row_stride,
     const int32_t* __restrict__ block_table, const int32_t* __restrict__ cu_seq_lens,
     int32_t num_reqs, int32_t max_blocks, int64_t num_tokens, int64_t num_blocks,
-    int64_t page_stride, int32_t block_size, int32_t head_dim) {
+    int64_t page_stride, int32_t block_size, int32_t head_dim, FastDiv upt_div) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t entries = (int64_t)num_reqs * max_blocks;
   const int64_t stride = (int64_t)gridDim.x * kDqWaves;
-  const int32_t cpt = head_dim / 16;  // 16-byte code chunks per token
+  const int32_t upt = head_dim / 8;  // 8-code units per token (upt_div divides by it)
   for (int64_t e = (int64_t)blockIdx.x * kDqWaves + threadIdx.x / kWave; e < entries;
        e += stride) {
     Run run;
@@ -129,43 +124,65 @@ __global__ __launch_bounds__(kDqThreads) void gather_indexer_k_dequant_kernel(
                          block_size, run))
       continue;
     const uint8_t* page = kv_cache + run.page * page_stride;
-    const u32x4* csrc = reinterpret_cast<const u32x4*>(page + run.first * head_dim);
+    const u32x2* csrc = reinterpret_cast<const u32x2*>(page + run.first * head_dim);
     const float* ssrc =
         reinterpret_cast<const float*>(page + (int64_t)block_size * head_dim) + run.first;
-    const int64_t chunks = run.rows * cpt;
-    for (int64_t c0 = 0; c0 < chunks; c0 += kWave * kDqUnroll) {
-      u32x4 v[kDqUnroll];
-      float s[kDqUnroll];
+    uint16_t* orow = out + run.row * out_row_stride;
+    const int32_t units = (int32_t)run.rows * upt;  // <= block_size * head_dim / 8
+    // runs of up to 64 tokens: lane l holds the scale of token l, and each
+    // unit takes its token's scale across lanes; longer runs load per unit
+    const bool lane_scales = run.rows <= kWave;
+    float my_scale = 0.0f;
+    if (lane_scales && lane < run.rows) my_scale = ssrc[lane];
+    for (int32_t c0 = 0; c0 < units; c0 += kWave * kIdxUnroll) {
+      u32x2 v[kIdxUnroll];
+      float sc[kIdxUnroll];
 #pragma unroll
-      for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t c = c0 + u * kWave + lane;
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-        s[u] = 0.0f;
-        if (c < chunks) {
-          v[u] = load_stream(csrc + c);
-          s[u] = ssrc[c / cpt];
+      for (int u = 0; u < kIdxUnroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        v[u] = u32x2{0u, 0u};
+        sc[u] = 0.0f;
+        if (c < units) {
+          v[u] = __builtin_nontemporal_load(csrc + c);
+          if (!lane_scales) sc[u] = ssrc[upt_div.div((uint32_t)c)];
+        }
+      }
+      if (lane_scales) {
+#pragma unroll
+        for (int u = 0; u < kIdxUnroll; ++u) {  // every lane takes part
+          const int32_t c = c0 + u * kWave + lane;
+          const int32_t t = c < units ? (int32_t)upt_div.div((uint32_t)c) : 0;
+          sc[u] = __uint_as_float(
+              (uint32_t)__builtin_amdgcn_ds_bpermute(t << 2, (int)__float_as_uint(my_scale)));
         }
       }
 #pragma unroll
-      for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t c = c0 + u * kWave + lane;
-        if (c >= chunks) continue;
-        const int64_t t = c / cpt;
-        u32x4 lo, hi;
-        dequant16_fp8<kF16>(v[u], s[u], lo, hi);
-        u32x4* dst = reinterpret_cast<u32x4*>(out + (run.row + t) * out_row_stride +
-                                              (c - t * cpt) * 16);
-        store_stream(dst, lo);
-        store_stream(dst + 1, hi);
+      for (int u = 0; u < kIdxUnroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        if (c >= units) continue;
+        const int32_t t = (int32_t)upt_div.div((uint32_t)c);
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].x, false);
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].x, true);
+        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].y, false);
+        const f32x2 g = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].y, true);
+        const float x = sc[u];
+        const u32x4 o = {narrow2<kF16>(a.x * x, a.y * x), narrow2<kF16>(b.x * x, b.y * x),
+                         narrow2<kF16>(d.x * x, d.y * x), narrow2<kF16>(g.x * x, g.y * x)};
+        store_stream(reinterpret_cast<u32x4*>(orow + (int64_t)t * out_row_stride +
+                                              (int64_t)(c - t * upt) * 8),
+                     o);
       }
     }
   }
 }
 
 // ------------------------------------------------------------- NVFP4 K/V
-// Unit = (table entry, side, head).  A 16-byte chunk holds the codes of two
-// consecutive blocks of one token head (32 elements -> 64 output bytes).
-template <bool kF16>
+// Work of a wave: one (table entry, side) -- the run's tokens, every head.
+// Lane unit = one half-block (4 code bytes, 8 elements of one token head) ->
+// 8 outputs (one 16-byte store); units run in output order, so a token's row
+// of H*D outputs is written by consecutive lanes and every wave store covers
+// 1 KB of it.
+template <int kD, bool kF16>
 __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_kernel(
     const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
     uint16_t* __restrict__ key_out, int64_t key_row_stride, uint16_t* __restrict__ value_out,
@@ -173,90 +190,75 @@ __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_kernel(
     const int32_t* __restrict__ cu_seq_lens, int32_t num_reqs, int32_t max_blocks,
     int64_t num_tokens, int32_t num_heads, int32_t head_size, int32_t block_size,
     int64_t num_blocks, int64_t page_stride, int32_t layout, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale) {
+    const float* __restrict__ v_scale, FastDiv upt_div, FastDiv hpt_div, FastDiv q4_div) {
   const int lane = threadIdx.x & (kWave - 1);
   const float ts_k = *k_scale, ts_v = *v_scale;
+  if constexpr (kD > 0) head_size = kD;
   const int32_t S = head_size / 16;
-  const int32_t q4 = S / 4;
-  const int32_t cpt = head_size / 32;  // 16-byte code chunks per token head
+  const int32_t hpt = head_size / 8;       // half-blocks per token head
+  const int32_t upt = num_heads * hpt;     // half-blocks per token (upt_div divides by it)
   const int64_t data_dim = head_size / 2;
   const int64_t data_per_side = (int64_t)num_heads * block_size * data_dim;
-  const int64_t units = (int64_t)num_reqs * max_blocks * 2 * num_heads;
+  const int64_t units_total = (int64_t)num_reqs * max_blocks * 2;
   const int64_t stride = (int64_t)gridDim.x * kDqWaves;
-  for (int64_t w = (int64_t)blockIdx.x * kDqWaves + threadIdx.x / kWave; w < units;
+  for (int64_t w = (int64_t)blockIdx.x * kDqWaves + threadIdx.x / kWave; w < units_total;
        w += stride) {
-    const int64_t e = w / (2 * num_heads);
-    const int32_t sh = (int32_t)(w - e * 2 * num_heads);
-    const int kv = sh >= num_heads;
-    const int32_t h = kv ? sh - num_heads : sh;
+    const int64_t e = w >> 1;
+    const int kv = (int)(w & 1);
     Run run;
     if (!table_entry_run(block_table, cu_seq_lens, e, max_blocks, num_tokens, num_blocks,
                          block_size, run))
       continue;
     const uint8_t* side = (kv ? value_cache : key_cache) + run.page * page_stride;
     const uint8_t* scales = side + data_per_side;
-    uint16_t* out = kv ? value_out : key_out;
+    uint16_t* orow = (kv ? value_out : key_out) + run.row * (kv ? value_row_stride : key_row_stride);
     const int64_t out_stride = kv ? value_row_stride : key_row_stride;
     const float ts = kv ? ts_v : ts_k;
-    const int64_t chunks = run.rows * cpt;
-    for (int64_t c0 = 0; c0 < chunks; c0 += kWave * kDqUnroll) {
-      u32x4 v[kDqUnroll];
-      uint32_t sc[kDqUnroll];  // the two block-scale bytes, low byte first
+    const int32_t units = (int32_t)run.rows * upt;
+    for (int32_t c0 = 0; c0 < units; c0 += kWave * kFp4Unroll) {
+      uint32_t v[kFp4Unroll], sb[kFp4Unroll];
 #pragma unroll
-      for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t c = c0 + u * kWave + lane;
-        v[u] = u32x4{0u, 0u, 0u, 0u};
-        sc[u] = 0u;
-        if (c < chunks) {
-          const int64_t t = c / cpt;
-          const int32_t wc = (int32_t)(c - t * cpt);
+      for (int u = 0; u < kFp4Unroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        v[u] = 0u;
+        sb[u] = 0u;
+        if (c < units) {
+          const int32_t t = (int32_t)upt_div.div((uint32_t)c);
+          const int32_t r = c - t * upt;
+          const int32_t h = kD > 0 ? r / (kD / 8) : (int32_t)hpt_div.div((uint32_t)r);
+          const int32_t hb = r - h * hpt;  // half-block within the head
+          const int32_t g = hb >> 1;
           const int64_t off = run.first + t;
           const int64_t row = layout == PKV_LAYOUT_HND ? (int64_t)h * block_size + off
                                                        : off * num_heads + h;
-          v[u] = load_stream(reinterpret_cast<const u32x4*>(side + row * data_dim) + wc);
-          const int32_t g0 = 2 * wc;
+          v[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const uint32_t*>(side + row * data_dim) + hb);
+          int64_t so;
           if (kv == 0) {
-            sc[u] = *reinterpret_cast<const uint16_t*>(scales + row * S + g0);
+            so = row * S + g;
           } else {
             // swizzled: (t', s') = ((off/4)*4 + g/(S/4), (g % (S/4))*4 + off%4)
-            const int64_t srow = (off >> 2) * 4 + g0 / q4;
-            const int64_t col = (int64_t)(g0 % q4) * 4 + (off & 3);
-            const int64_t base = layout == PKV_LAYOUT_HND ? ((int64_t)h * block_size + srow) * S
-                                                          : (srow * num_heads + h) * S;
-            const int32_t g1 = g0 + 1;
-            const int64_t srow1 = (off >> 2) * 4 + g1 / q4;
-            const int64_t col1 = (int64_t)(g1 % q4) * 4 + (off & 3);
-            const int64_t base1 = layout == PKV_LAYOUT_HND
-                                      ? ((int64_t)h * block_size + srow1) * S
-                                      : (srow1 * num_heads + h) * S;
-            sc[u] = (uint32_t)scales[base + col] | ((uint32_t)scales[base1 + col1] << 8);
+            const int32_t gq = kD > 0 ? g / (kD / 64) : (int32_t)q4_div.div((uint32_t)g);
+            const int32_t gr = g - gq * (S / 4);
+            const int64_t srow = (off >> 2) * 4 + gq;
+            const int64_t col = (int64_t)gr * 4 + (off & 3);
+            so = (layout == PKV_LAYOUT_HND ? ((int64_t)h * block_size + srow) * S
+                                           : (srow * num_heads + h) * S) + col;
           }
+          sb[u] = scales[so];
         }
       }
 #pragma unroll
-      for (int u = 0; u < kDqUnroll; ++u) {
-        const int64_t c = c0 + u * kWave + lane;
-        if (c >= chunks) continue;
-        const int64_t t = c / cpt;
-        const int32_t wc = (int32_t)(c - t * cpt);
-        const float sfd0 = __builtin_amdgcn_cvt_f32_fp8((int)sc[u], 0);
-        const float sfd1 = __builtin_amdgcn_cvt_f32_fp8((int)sc[u], 1);
-        const uint32_t cw[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        uint32_t o[16];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float sfd = q < 2 ? sfd0 : sfd1;  // dwords 0-1: block g0, 2-3: block g0+1
-          // byte b of the dword holds elements 2b (low nibble) and 2b+1
-          o[q * 4 + 0] = fp4_pair<0, kF16>(cw[q], sfd, ts);
-          o[q * 4 + 1] = fp4_pair<1, kF16>(cw[q], sfd, ts);
-          o[q * 4 + 2] = fp4_pair<2, kF16>(cw[q], sfd, ts);
-          o[q * 4 + 3] = fp4_pair<3, kF16>(cw[q], sfd, ts);
-        }
-        u32x4* dst = reinterpret_cast<u32x4*>(out + (run.row + t) * out_stride +
-                                              (int64_t)h * head_size + (int64_t)wc * 32);
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          store_stream(dst + k, u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]});
+      for (int u = 0; u < kFp4Unroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        if (c >= units) continue;
+        const int32_t t = (int32_t)upt_div.div((uint32_t)c);
+        const float sfd = __builtin_amdgcn_cvt_f32_fp8((int)sb[u], 0);
+        const u32x4 o = {fp4_pair<0, kF16>(v[u], sfd, ts), fp4_pair<1, kF16>(v[u], sfd, ts),
+                         fp4_pair<2, kF16>(v[u], sfd, ts), fp4_pair<3, kF16>(v[u], sfd, ts)};
+        store_stream(reinterpret_cast<u32x4*>(orow + (int64_t)t * out_stride +
+                                              (int64_t)(c - t * upt) * 8),
+                     o);
       }
     }
   }
@@ -294,19 +296,26 @@ int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stre
   hipLaunchKernelGGL(kernel, dim3((unsigned)dq_blocks(entries)), dim3(kDqThreads), 0, stream,
                      a.kv_cache, a.out, a.out_row_stride, a.block_table, a.cu_seq_lens,
                      a.num_reqs, a.max_blocks_per_req, a.num_tokens, a.num_blocks,
-                     a.cache_block_stride, a.block_size, a.head_dim);
+                     a.cache_block_stride, a.block_size, a.head_dim,
+                     FastDiv::make((uint32_t)(a.head_dim / 8)));
   return (int)hipGetLastError();
 }
 
 int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream) {
-  const int64_t units = (int64_t)a.num_reqs * a.max_blocks_per_req * 2 * a.num_heads;
-  auto kernel = a.out_dtype == PKV_DTYPE_F16 ? gather_kv_fp4_dequant_kernel<true>
-                                             : gather_kv_fp4_dequant_kernel<false>;
+  const int64_t units = (int64_t)a.num_reqs * a.max_blocks_per_req * 2;
+  const bool f16 = a.out_dtype == PKV_DTYPE_F16;
+  auto kernel = f16 ? gather_kv_fp4_dequant_kernel<0, true> : gather_kv_fp4_dequant_kernel<0, false>;
+  if (a.head_size == 64) kernel = f16 ? gather_kv_fp4_dequant_kernel<64, true> : gather_kv_fp4_dequant_kernel<64, false>;
+  if (a.head_size == 128) kernel = f16 ? gather_kv_fp4_dequant_kernel<128, true> : gather_kv_fp4_dequant_kernel<128, false>;
+  if (a.head_size == 256) kernel = f16 ? gather_kv_fp4_dequant_kernel<256, true> : gather_kv_fp4_dequant_kernel<256, false>;
+  const uint32_t hpt = (uint32_t)(a.head_size / 8);
   hipLaunchKernelGGL(kernel, dim3((unsigned)dq_blocks(units)), dim3(kDqThreads), 0, stream,
                      a.key_cache, a.value_cache, a.key_out, a.key_row_stride, a.value_out,
                      a.value_row_stride, a.block_table, a.cu_seq_lens, a.num_reqs,
                      a.max_blocks_per_req, a.num_tokens, a.num_heads, a.head_size, a.block_size,
-                     a.num_blocks, a.page_stride, a.layout, a.k_scale, a.v_scale);
+                     a.num_blocks, a.page_stride, a.layout, a.k_scale, a.v_scale,
+                     FastDiv::make(hpt * (uint32_t)a.num_heads), FastDiv::make(hpt),
+                     FastDiv::make((uint32_t)(a.head_size / 64)));
   return (int)hipGetLastError();
 }
 

@@ -27,26 +27,9 @@ namespace pkv {
 
 namespace {
 
-#ifndef PKV_GATHER_THREADS
-#define PKV_GATHER_THREADS 256
-#endif
-constexpr int kGatherThreads = PKV_GATHER_THREADS;
+constexpr int kGatherThreads = 256;
 constexpr int kGatherWaves = kGatherThreads / kWave;
-#ifndef PKV_GATHER_UNROLL
-#define PKV_GATHER_UNROLL 8
-#endif
-constexpr int kGatherUnroll = PKV_GATHER_UNROLL;  // 16-byte chunks per lane in flight
-#ifndef PKV_GATHER_SUB
-#define PKV_GATHER_SUB 0  // tokens per wave in the direct kernel (0: the whole page run)
-#endif
-#ifndef PKV_GATHER_NT_STORE
-#define PKV_GATHER_NT_STORE 1
-#endif
-
-__device__ __forceinline__ void store_codes(u32x4* p, u32x4 v) {
-  if constexpr (PKV_GATHER_NT_STORE) store_stream(p, v);
-  else *p = v;
-}
+constexpr int kGatherUnroll = 8;  // 16-byte chunks per lane in flight
 
 // Copy tokens [j*B + o_lo, j*B + o_hi) of a request whose rows are
 // [start, end) of the output, clipped to the request: page offsets
@@ -95,7 +78,7 @@ __device__ __forceinline__ void copy_run(const uint8_t* __restrict__ kv_cache,
 #pragma unroll
     for (int u = 0; u < kGatherUnroll; ++u) {
       const int64_t c = c0 + u * kWave + lane;
-      if (c < chunks) store_codes(cdst + c, v[u]);
+      if (c < chunks) store_stream(cdst + c, v[u]);
     }
   }
   if (has_scale) sdst[lane] = sv;
@@ -114,20 +97,14 @@ __global__ __launch_bounds__(kGatherThreads) void gather_indexer_k_fp8_direct_ke
     int64_t num_tokens, int64_t num_blocks, int64_t page_stride, int32_t block_size,
     int32_t head_dim) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int32_t sub = PKV_GATHER_SUB > 0 && PKV_GATHER_SUB < block_size ? PKV_GATHER_SUB : block_size;
-  const int32_t nsub = (block_size + sub - 1) / sub;
-  const int64_t units = (int64_t)num_reqs * max_blocks * nsub;
+  const int64_t entries = (int64_t)num_reqs * max_blocks;
   const int64_t stride = (int64_t)gridDim.x * kGatherWaves;
-  for (int64_t w = (int64_t)blockIdx.x * kGatherWaves + threadIdx.x / kWave; w < units;
-       w += stride) {
-    const int64_t e = w / nsub;
-    const int32_t part = (int32_t)(w - e * nsub);
+  for (int64_t e = (int64_t)blockIdx.x * kGatherWaves + threadIdx.x / kWave; e < entries;
+       e += stride) {
     const int32_t r = (int32_t)(e / max_blocks);
     const int32_t j = (int32_t)(e - (int64_t)r * max_blocks);
-    const int32_t o_lo = part * sub;
-    const int32_t o_hi = o_lo + sub < block_size ? o_lo + sub : block_size;
     copy_run(kv_cache, k_fp8, k_scale, cu_seq_lens[r], cu_seq_lens[r + 1], block_table[e], j,
-             o_lo, o_hi, num_tokens, num_blocks, page_stride, block_size, head_dim, lane);
+             0, block_size, num_tokens, num_blocks, page_stride, block_size, head_dim, lane);
   }
 }
 
@@ -211,9 +188,7 @@ int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream) {
   const int64_t run_bound = (a.num_tokens + a.block_size - 1) / a.block_size + a.num_reqs;
   const bool direct = PKV_GATHER_MODE == 2 || (PKV_GATHER_MODE == 0 && table <= 2 * run_bound);
   if (direct) {
-    const int32_t sub = PKV_GATHER_SUB > 0 && PKV_GATHER_SUB < a.block_size ? PKV_GATHER_SUB : a.block_size;
-    const int64_t units = table * ((a.block_size + sub - 1) / sub);
-    int64_t blocks = (units + kGatherWaves - 1) / kGatherWaves;
+    int64_t blocks = (table + kGatherWaves - 1) / kGatherWaves;
     if (blocks > kGatherMaxBlocks) blocks = kGatherMaxBlocks;
     hipLaunchKernelGGL(gather_indexer_k_fp8_direct_kernel, dim3((unsigned)blocks),
                        dim3(kGatherThreads), 0, stream, a.kv_cache, a.k_fp8, a.k_scale,

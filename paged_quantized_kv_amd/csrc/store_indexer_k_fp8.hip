@@ -28,21 +28,9 @@ namespace pkv {
 
 namespace {
 
-#ifndef PKV_STORE8_THREADS
-#define PKV_STORE8_THREADS 256
-#endif
-constexpr int kStoreThreads = PKV_STORE8_THREADS;
+constexpr int kStoreThreads = 256;
 
-#ifndef PKV_STORE8_UNROLL
-#define PKV_STORE8_UNROLL 2
-#endif
-constexpr int kStoreUnroll = PKV_STORE8_UNROLL;  // token groups per wave in flight
-#ifndef PKV_STORE8_NT
-#define PKV_STORE8_NT 0  // nontemporal code stores
-#endif
-#ifndef PKV_STORE8_NT_SCALE
-#define PKV_STORE8_NT_SCALE 0  // nontemporal scale stores
-#endif
+constexpr int kStoreUnroll = 2;  // token groups per wave in flight
 
 // kLanes lanes per token (a power of two), each holding kChunks runs of 8
 // elements: lane l of a token takes elements [8*(l + c*kLanes), +8), so the
@@ -112,15 +100,10 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
       u32x2 codes;
       codes.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
       codes.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
-      u32x2* dst = reinterpret_cast<u32x2*>(page_base + off * head_dim + e0);
-      if constexpr (PKV_STORE8_NT) __builtin_nontemporal_store(codes, dst);
-      else *dst = codes;
+      *reinterpret_cast<u32x2*>(page_base + off * head_dim + e0) = codes;
     }
-    if (part == 0) {
-      float* dst = reinterpret_cast<float*>(page_base + (int64_t)block_size * head_dim + off * 4);
-      if constexpr (PKV_STORE8_NT_SCALE) __builtin_nontemporal_store(s, dst);
-      else *dst = s;
-    }
+    if (part == 0)
+      *reinterpret_cast<float*>(page_base + (int64_t)block_size * head_dim + off * 4) = s;
   }
 }
 

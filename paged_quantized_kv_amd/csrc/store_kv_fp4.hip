@@ -55,10 +55,7 @@ namespace pkv {
 
 namespace {
 
-#ifndef PKV_FP4_THREADS
-#define PKV_FP4_THREADS 256
-#endif
-constexpr int kFp4Threads = PKV_FP4_THREADS;
+constexpr int kFp4Threads = 256;
 constexpr int kFp4Waves = kFp4Threads / kWave;
 
 #ifndef PKV_FP4_UNROLL
@@ -66,30 +63,11 @@ constexpr int kFp4Waves = kFp4Threads / kWave;
 #endif
 constexpr int kFp4Unroll = PKV_FP4_UNROLL;  // half-blocks per lane in flight (generic kernel)
 
-#ifndef PKV_FP4_TILE
-#define PKV_FP4_TILE 16
-#endif
-constexpr int kFp4Tile = PKV_FP4_TILE;  // tokens per wave item (tile kernel)
-#ifndef PKV_FP4_ITEMS
-#define PKV_FP4_ITEMS 1
-#endif
-constexpr int kFp4Items = PKV_FP4_ITEMS;  // items per wave whose loads are in flight together
+constexpr int kFp4Tile = 16;  // tokens per wave item (tile kernel)
+// Items per wave whose loads are in flight together; 2 or 4 cut occupancy
+// more than they added bytes in flight.
+constexpr int kFp4Items = 1;
 
-#ifndef PKV_FP4_NT_STORE
-#define PKV_FP4_NT_STORE 1
-#endif
-#ifndef PKV_FP4_NT_SCALE
-#define PKV_FP4_NT_SCALE 0
-#endif
-#ifndef PKV_FP4_ORDER
-#define PKV_FP4_ORDER 0
-#endif
-#ifndef PKV_FP4_WPE
-#define PKV_FP4_WPE 0
-#endif
-#ifndef PKV_FP4_NT_LOAD
-#define PKV_FP4_NT_LOAD 1
-#endif
 
 struct Div {
   // n / d and n % d for a positive divisor that may or may not be a power of two
@@ -169,19 +147,19 @@ __device__ __forceinline__ uint32_t nvfp4_half_block(const float (&x)[8], float 
   return packed;
 }
 
-__device__ __forceinline__ u32x4 load_src(const u32x4* p) {
-  if constexpr (PKV_FP4_NT_LOAD) return load_stream(p);
-  else return *p;
-}
+// K/V rows are read once: nontemporal loads.
+__device__ __forceinline__ u32x4 load_src(const u32x4* p) { return load_stream(p); }
 
+// Code chunks fill whole lines: nontemporal stores (about 7% faster here than
+// write-back ones, and they leave the next kernel fewer dirty lines).
 __device__ __forceinline__ void store_codes16(uint8_t* p, u32x4 v) {
-  if constexpr (PKV_FP4_NT_STORE) store_stream(reinterpret_cast<u32x4*>(p), v);
-  else *reinterpret_cast<u32x4*>(p) = v;
+  store_stream(reinterpret_cast<u32x4*>(p), v);
 }
 
+// Scale dwords cover parts of lines that other waves complete: plain stores,
+// merged in L2 (nontemporal ones measured slower).
 __device__ __forceinline__ void store_scale4(uint8_t* p, uint32_t v) {
-  if constexpr (PKV_FP4_NT_SCALE) __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
-  else *reinterpret_cast<uint32_t*>(p) = v;
+  *reinterpret_cast<uint32_t*>(p) = v;
 }
 
 // Byte offset of V scale (off, g) inside its page side's scale region:
@@ -199,11 +177,7 @@ __device__ __forceinline__ int64_t v_scale_offset(int64_t off, int32_t g, int32_
 
 // ------------------------------------------------------------------ tile kernel
 template <int kD, bool kF16>
-__global__ __launch_bounds__(kFp4Threads)
-#if PKV_FP4_WPE
-__attribute__((amdgpu_waves_per_eu(PKV_FP4_WPE)))
-#endif
-void store_kv_fp4_tile_kernel(
+__global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_tile_kernel(
     const uint16_t* __restrict__ key, int64_t key_row_stride, const uint16_t* __restrict__ value,
     int64_t value_row_stride, uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
     const int64_t* __restrict__ slot_mapping, int64_t num_tokens, int64_t num_items,
@@ -233,11 +207,7 @@ void store_kv_fp4_tile_kernel(
   const int64_t data_per_side = (int64_t)num_heads * block_size * (kD / 2);
   const int32_t sides_heads = 2 * num_heads;
 
-#ifndef PKV_FP4_XCD
-#define PKV_FP4_XCD 1
-#endif
-  const int64_t first_block = PKV_FP4_XCD ? xcd_contiguous_block() : blockIdx.x;
-  for (int64_t lb = first_block; lb < num_logical_blocks; lb += gridDim.x) {
+  for (int64_t lb = xcd_contiguous_block(); lb < num_logical_blocks; lb += gridDim.x) {
     // this wave's kFp4Items consecutive items, each a (tile, side, head)
     int64_t t0[kFp4Items], my_slot[kFp4Items];
     int kv[kFp4Items];
@@ -250,13 +220,8 @@ void store_kv_fp4_tile_kernel(
       valid[u] = item < num_items;  // wave-uniform
       const int64_t tile = item / sides_heads;
       const int32_t sh = (int32_t)(item - tile * sides_heads);
-#if PKV_FP4_ORDER
-      kv[u] = sh & 1;
-      h[u] = sh >> 1;
-#else
       kv[u] = sh >= num_heads;
       h[u] = kv[u] ? sh - num_heads : sh;
-#endif
       t0[u] = tile * kFp4Tile;
       // slot of token t0 + (lane % 16); tokens past the end have slot -1
       const int64_t my_t = t0[u] + (lane & (kFp4Tile - 1));

@@ -84,3 +84,29 @@ def test_markstein_quotients_equal_ieee_division():
     assert bad6 == 0, f"{bad6} significands where the corrected t/6 differs"
     assert bad8 == 0, f"{bad8} significand pairs where the corrected x/s differs"
     assert bad16 == 0, f"{bad16} fp16 significand pairs where the corrected x/s differs"
+
+
+def test_invariant_integer_division_by_multiplication():
+    """The kernels divide unit indices n < 2^31 by a launch-constant d with
+    q = (n * m) >> (31 + l), l = ceil(log2 d), m = ceil(2^(31+l) / d)
+    (Granlund and Montgomery, PLDI 1994, Theorem 4.2).  Checked here against
+    integer division at the edges of every residue pattern that matters: all
+    n near multiples of d and near 2^31, for every divisor up to 4096 and a
+    spread of larger ones."""
+    import numpy as np
+
+    def magic(d):
+        l = (d - 1).bit_length()
+        return (2 ** (31 + l) + d - 1) // d, 31 + l
+
+    rng = np.random.default_rng(0)
+    divisors = list(range(1, 4097)) + [int(x) for x in rng.integers(4097, 2 ** 31, 2000)]
+    for d in divisors:
+        m, sh = magic(d)
+        assert m < 2 ** 32
+        k = np.unique(np.concatenate([np.arange(0, 64), rng.integers(0, (2 ** 31 - 1) // d + 1, 64),
+                                      [(2 ** 31 - 1) // d]])).astype(np.int64)
+        n = np.concatenate([k * d, k * d + d - 1, k * d - 1, [2 ** 31 - 1]])
+        n = n[(n >= 0) & (n < 2 ** 31)].astype(object)
+        q = [(int(v) * m) >> sh for v in n]
+        assert q == [int(v) // d for v in n], d
