@@ -88,6 +88,8 @@ def _load():
     lib.oracle_gather_kv_fp4_dequant.argtypes = [P, P, P, i64, P, i64, i32, P, P, i32, i32,
                                                  i64, i32, i32, i32, i64, i64, i32, f32, f32]
     lib.oracle_gather_kv_fp4_dequant.restype = None
+    lib.oracle_fp8_mqa_logits.argtypes = [P, P, P, P, P, P, P, i64, i64, i32, i32, i64, i32]
+    lib.oracle_fp8_mqa_logits.restype = None
     _lib = lib
     return lib
 
@@ -269,3 +271,27 @@ def gather_kv_fp4_dequant(kv_cache, key_out, value_out, block_table, cu_seq_lens
         _ptr(value_out), value_out.shape[1], OUT_DTYPES[dtype], _ptr(block_table),
         _ptr(cu_seq_lens), num_reqs, maxb, T, num_heads, head_size, block_size,
         kv_cache.shape[0], 2 * side_bytes, layout, float(k_scale), float(v_scale))
+
+
+# ----------------------------------------------------------------- indexer logits
+def fp8_mqa_logits(q_codes, k_codes, k_scale, weights, ks, ke, logits):
+    """Indexer scores in binary64 (in place into logits, float64 [M, row_cols]).
+
+    q_codes uint8 [M, H, D]; k_codes uint8 [N, D]; k_scale float32 [N];
+    weights float32 [M, H]; ks, ke int32 [M].  Row i, column j - ks[i] gets
+    sum_h weights[i,h] * relu(k_scale[j] * q[i,h] . k[j]) for j in [ks, ke).
+    """
+    _need(q_codes, np.uint8, "q_codes")
+    _need(k_codes, np.uint8, "k_codes")
+    _need(k_scale, np.float32, "k_scale")
+    _need(weights, np.float32, "weights")
+    _need(ks, np.int32, "ks")
+    _need(ke, np.int32, "ke")
+    _need(logits, np.float64, "logits")
+    M, H, D = q_codes.shape
+    N = k_codes.shape[0]
+    assert k_codes.shape == (N, D) and k_scale.shape == (N,) and weights.shape == (M, H)
+    assert ks.shape == (M,) and ke.shape == (M,) and logits.shape[0] == M
+    _load().oracle_fp8_mqa_logits(_ptr(q_codes), _ptr(k_codes), _ptr(k_scale), _ptr(weights),
+                                  _ptr(ks), _ptr(ke), _ptr(logits), logits.shape[1],
+                                  logits.shape[1], M, H, N, D)

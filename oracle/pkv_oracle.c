@@ -613,3 +613,50 @@ void oracle_gather_kv_fp4_dequant(const uint8_t *key_cache, const uint8_t *value
         }
     }
 }
+
+/* ================================================================== */
+/* Indexer logits on the gathered keys (the op the integration PR hands */
+/* k_fp8 and k_scale.view(float32) to, fp8_mqa_logits; its body is not  */
+/* on the pages -- the reading is the lightning-indexer score).         */
+/* ================================================================== */
+
+/* For query token i and key j in [ks[i], ke[i]) (clipped to [0, num_k)  */
+/* and to the row's first `row_cols` columns):                           */
+/*   logits[i*row_stride + (j - ks[i])] =                                 */
+/*       sum_h weights[i*H + h] * max(0, k_scale[j] * sum_d q[i,h,d]*k[j,d]) */
+/* with q and k E4M3 codes decoded exactly.  Worked in binary64: every   */
+/* product of two E4M3 values is exact, and a 128-term dot product of   */
+/* them spans under 53 bits, so the dot product is exact; the rest is   */
+/* binary64 arithmetic (relative error ~2^-50).  Entries outside the    */
+/* ranges are left untouched.                                           */
+void oracle_fp8_mqa_logits(const uint8_t *q, const uint8_t *k, const float *k_scale,
+                           const float *weights, const int32_t *ks, const int32_t *ke,
+                           double *logits, int64_t row_stride, int64_t row_cols,
+                           int32_t num_q, int32_t num_heads, int64_t num_k,
+                           int32_t head_dim)
+{
+    int32_t i;
+    for (i = 0; i < num_q; ++i) {
+        int64_t j, lo = ks[i], hi = ke[i];
+        if (lo < 0) lo = 0;
+        if (hi > num_k) hi = num_k;
+        for (j = lo; j < hi; ++j) {
+            double acc = 0.0;
+            int32_t h;
+            if (j - ks[i] >= row_cols)
+                continue;
+            for (h = 0; h < num_heads; ++h) {
+                const uint8_t *qh = q + ((int64_t)i * num_heads + h) * head_dim;
+                const uint8_t *kj = k + j * head_dim;
+                double dot = 0.0, s;
+                int32_t d;
+                for (d = 0; d < head_dim; ++d)
+                    dot += (double)oracle_e4m3_decode(qh[d]) * (double)oracle_e4m3_decode(kj[d]);
+                s = (double)k_scale[j] * dot;
+                if (s > 0.0)
+                    acc += (double)weights[(int64_t)i * num_heads + h] * s;
+            }
+            logits[(int64_t)i * row_stride + (j - ks[i])] = acc;
+        }
+    }
+}
