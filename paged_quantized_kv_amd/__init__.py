@@ -18,7 +18,8 @@ import torch
 
 __all__ = [
     "pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
-    "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant", "pkv_diag_narrow",
+    "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant", "pkv_fp8_mqa_logits",
+    "pkv_diag_narrow",
     "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "PkvError", "LAYOUT_HND", "LAYOUT_NHD",
     "library_path", "abi_version",
 ]
@@ -78,10 +79,12 @@ def _load():
                                               i32, i32, i32, i64, i64, i32, P, P, P]
     lib.pkv_diag_encode_e4m3.argtypes = [P, P, i64, P]
     lib.pkv_diag_narrow.argtypes = [P, P, i64, i32, P]
+    lib.pkv_fp8_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P, i64, i64, i32, i32, i64, i32, P]
     lib.pkv_diag_encode_e2m1.argtypes = [P, P, i64, P]
     for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
                  "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
-                 "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "pkv_diag_narrow"):
+                 "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "pkv_diag_narrow",
+                 "pkv_fp8_mqa_logits"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -370,3 +373,50 @@ def pkv_diag_narrow(x, out, stream=None):
     if out.numel() != x.numel():
         raise ValueError("out must have x.numel() elements")
     _check(_lib.pkv_diag_narrow(x.data_ptr(), out.data_ptr(), x.numel(), dt, _stream(stream)))
+
+
+def pkv_fp8_mqa_logits(q, k, k_scale, weights, ks, ke, logits, stream=None):
+    """Indexer scores of query tokens against the gathered keys.
+
+    q:        float8_e4m3fn or uint8 [num_q, num_heads, 128] (heads and elements
+              contiguous, token stride free).
+    k:        float8_e4m3fn or uint8 [num_k, 128] contiguous (the gather's k_fp8).
+    k_scale:  float32 [num_k] (or the gather's uint8 [num_k, 4] scale bytes).
+    weights:  float32 [num_q, num_heads] contiguous.
+    ks, ke:   int32 [num_q]: key range of each query token.
+    logits:   float32 [num_q, row_cols] (row stride free), written at column
+              j - ks[i] for j in [ks[i], ke[i]).
+    """
+    for t, n in ((q, "q"), (k, "k")):
+        _dev(t, n)
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must be uint8 or float8_e4m3fn")
+    _dev(k_scale, "k_scale")
+    _dev(weights, "weights", torch.float32)
+    _dev(ks, "ks", torch.int32)
+    _dev(ke, "ke", torch.int32)
+    _dev(logits, "logits", torch.float32)
+    for t, n in ((k, "k"), (k_scale, "k_scale"), (weights, "weights"), (ks, "ks"), (ke, "ke")):
+        _contig(t, n)
+    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+        raise ValueError("q must be [num_q, num_heads, head_dim] with contiguous heads")
+    num_q, num_heads, head_dim = q.shape
+    if k.dim() != 2 or k.shape[1] != head_dim:
+        raise ValueError("k must be [num_k, head_dim]")
+    num_k = k.shape[0]
+    if k_scale.dtype == torch.uint8:
+        ok = tuple(k_scale.shape) == (num_k, SCALE_BYTES)
+    else:
+        ok = k_scale.dtype == torch.float32 and k_scale.numel() == num_k
+    if not ok:
+        raise ValueError("k_scale must be float32 [num_k] or uint8 [num_k, 4]")
+    if tuple(weights.shape) != (num_q, num_heads):
+        raise ValueError("weights must be [num_q, num_heads]")
+    if ks.numel() != num_q or ke.numel() != num_q:
+        raise ValueError("ks and ke must have num_q entries")
+    if logits.dim() != 2 or logits.shape[0] != num_q or logits.stride(1) != 1:
+        raise ValueError("logits must be [num_q, row_cols] with contiguous rows")
+    _check(_lib.pkv_fp8_mqa_logits(
+        q.data_ptr(), q.stride(0) * q.element_size(), k.data_ptr(), k_scale.data_ptr(),
+        weights.data_ptr(), ks.data_ptr(), ke.data_ptr(), logits.data_ptr(), logits.stride(0),
+        logits.shape[1], num_q, num_heads, num_k, head_dim, _stream(stream)))

@@ -26,6 +26,7 @@ SOURCES = [
     "store_indexer_k_fp8.hip",
     "store_kv_fp4.hip",
     "gather_dequant.hip",
+    "mqa_logits.hip",
     "diag_codecs.hip",
 ]
 

@@ -108,7 +108,24 @@ struct GatherFp4DequantArgs {
   const float* v_scale;
 };
 
+struct MqaLogitsArgs {
+  const uint8_t* q;
+  int64_t q_token_stride;  // bytes
+  const uint8_t* k;
+  const float* k_scale;
+  const float* weights;
+  const int32_t* ks;
+  const int32_t* ke;
+  float* logits;
+  int64_t row_stride;  // elements
+  int64_t row_cols;
+  int32_t num_q;
+  int32_t num_heads;
+  int64_t num_k;
+};
+
 int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream);
+int launch_fp8_mqa_logits(const MqaLogitsArgs& a, hipStream_t stream);
 int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stream);
 int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream);
 int launch_store_indexer_k_fp8(const StoreFp8Args& a, hipStream_t stream);

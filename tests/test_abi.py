@@ -26,7 +26,7 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     for s in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
               "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
-              "pkv_last_error", "pkv_abi_version"):
+              "pkv_fp8_mqa_logits", "pkv_last_error", "pkv_abi_version"):
         assert s in syms
 
 
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
     for s in declared_symbols():
         assert s in exported, s
         assert getattr(lib, s) is not None
-    assert pkv.abi_version() == 3
+    assert pkv.abi_version() == 4
 
 
 def lib():
@@ -205,6 +205,37 @@ def test_gather_fp4_dequant_validation(kw, code, msg):
 
 def test_gather_fp4_dequant_empty_is_ok():
     assert g4(T=0, kc=0, vc=0, ko=0, vo=0, block_table=0, cu=0, kscale=0, vscale=0) == PKV_OK
+
+
+def lg(**kw):
+    a = dict(q=A, qst=8192, k=A, kscale=A, w=A, ks=A, ke=A, out=A, rst=1000, rcols=1000, M=8,
+             H=64, N=100, D=128)
+    a.update(kw)
+    return lib().pkv_fp8_mqa_logits(a["q"], a["qst"], a["k"], a["kscale"], a["w"], a["ks"],
+                                    a["ke"], a["out"], a["rst"], a["rcols"], a["M"], a["H"],
+                                    a["N"], a["D"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(D=64, qst=4096), PKV_EUNSUPPORTED, "head_dim must be 128"),
+    (dict(H=24), PKV_EUNSUPPORTED, "num_heads"),
+    (dict(H=128, qst=16384), PKV_EUNSUPPORTED, "num_heads"),
+    (dict(qst=8000), PKV_EINVAL, "q_token_stride"),
+    (dict(qst=8200), PKV_EALIGN, "multiple of 16"),
+    (dict(rst=999), PKV_EINVAL, "row_stride"),
+    (dict(M=-1), PKV_EINVAL, "num_q"),
+    (dict(k=0), PKV_EINVAL, "null"),
+    (dict(q=A + 8), PKV_EALIGN, "16-byte"),
+    (dict(out=A + 2), PKV_EALIGN, "4-byte"),
+])
+def test_mqa_logits_validation(kw, code, msg):
+    assert lg(**kw) == code
+    assert msg in last_error()
+
+
+def test_mqa_logits_empty_is_ok():
+    assert lg(M=0, q=0, k=0, kscale=0, w=0, ks=0, ke=0, out=0) == PKV_OK
+    assert lg(N=0, q=0, k=0, kscale=0, w=0, ks=0, ke=0, out=0) == PKV_OK
 
 
 def test_diag_validation():

@@ -291,3 +291,47 @@ def prefill_fp4(num_reqs=256, req_len=1000, H=8, D=128, B=16, seed=1005) -> Fp4W
     num_blocks = 1 << int(np.ceil(np.log2(need)))
     return _fp4(f"prefill_fp4_{num_reqs}x{req_len}", seed, None, H, D, B, num_blocks,
                 lens=[req_len] * num_reqs, drop_frac=0.0)
+
+
+@dataclass
+class MqaLogitsCase:
+    """Inputs of the indexer logits: fp8 query rows against fp8 keys."""
+    q: np.ndarray          # uint8 E4M3 codes [M, H, 128]
+    k: np.ndarray          # uint8 E4M3 codes [N, 128]
+    k_scale: np.ndarray    # float32 [N]
+    weights: np.ndarray    # float32 [M, H]
+    ks: np.ndarray         # int32 [M]
+    ke: np.ndarray         # int32 [M]
+
+
+def _e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Codes of float32 values already inside the E4M3 range (torch's cast)."""
+    import torch
+    t = torch.from_numpy(np.clip(x, -448, 448).astype(np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def mqa_logits_case(seed, num_q, num_heads, num_k, causal_lens=None, head_dim=128):
+    """Query codes from N(0,1)*8, key codes from N(0,1)*64 (so both span most
+    E4M3 binades), key scales uniform in [0.001, 0.01] (the size amax/448 has
+    for unit-normal keys), weights N(0,1)/8.  With causal_lens the queries
+    and keys are the tokens of those requests in order and token i of a
+    request sees keys [request start, i]; otherwise each query gets a random
+    range inside [0, num_k)."""
+    g = rng(seed)
+    if causal_lens is not None:
+        lens = [int(n) for n in causal_lens]
+        num_q = num_k = sum(lens)
+        ks = np.concatenate([np.full(n, s) for n, s in zip(lens, np.cumsum([0] + lens[:-1]))]
+                            ).astype(np.int32) if num_q else np.zeros(0, np.int32)
+        ke = (ks + np.concatenate([np.arange(1, n + 1) for n in lens])).astype(np.int32) \
+            if num_q else np.zeros(0, np.int32)
+    else:
+        a = g.integers(0, num_k + 1, size=num_q)
+        b = g.integers(0, num_k + 1, size=num_q)
+        ks, ke = np.minimum(a, b).astype(np.int32), np.maximum(a, b).astype(np.int32)
+    q = _e4m3_codes(normal_f32(g, (num_q, num_heads, head_dim)) * np.float32(8))
+    k = _e4m3_codes(normal_f32(g, (num_k, head_dim)) * np.float32(64))
+    k_scale = g.uniform(0.001, 0.01, size=num_k).astype(np.float32)
+    weights = (normal_f32(g, (num_q, num_heads)) / np.float32(8)).astype(np.float32)
+    return MqaLogitsCase(q, k, k_scale, weights, ks, ke)
