@@ -90,6 +90,9 @@ def _load():
     lib.oracle_gather_kv_fp4_dequant.restype = None
     lib.oracle_fp8_mqa_logits.argtypes = [P, P, P, P, P, P, P, i64, i64, i32, i32, i64, i32]
     lib.oracle_fp8_mqa_logits.restype = None
+    lib.oracle_paged_attention_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                                  i32, i64, ctypes.c_double, f32, f32]
+    lib.oracle_paged_attention_decode.restype = None
     _lib = lib
     return lib
 
@@ -295,3 +298,30 @@ def fp8_mqa_logits(q_codes, k_codes, k_scale, weights, ks, ke, logits):
     _load().oracle_fp8_mqa_logits(_ptr(q_codes), _ptr(k_codes), _ptr(k_scale), _ptr(weights),
                                   _ptr(ks), _ptr(ke), _ptr(logits), logits.shape[1],
                                   logits.shape[1], M, H, N, D)
+
+
+# ----------------------------------------------------------------- paged decode attention
+def paged_attention_decode(query_bits, key_cache, value_cache, block_tables, context_lens,
+                           num_kv_heads, scale, k_scale, v_scale):
+    """Decode attention over fp8 pages in binary64; returns out float64 [S, H, D].
+
+    query_bits uint16 bf16 patterns [S, H, D]; key_cache uint8
+    [num_blocks, KVH, D/16, B, 16]; value_cache uint8 [num_blocks, KVH, D, B];
+    block_tables int32 [S, maxb]; context_lens int32 [S].
+    """
+    _need(query_bits, np.uint16, "query_bits")
+    _need(key_cache, np.uint8, "key_cache")
+    _need(value_cache, np.uint8, "value_cache")
+    _need(block_tables, np.int32, "block_tables")
+    _need(context_lens, np.int32, "context_lens")
+    S, H, D = query_bits.shape
+    nb, kvh, d16, B, x = key_cache.shape
+    assert kvh == num_kv_heads and d16 * 16 == D and x == 16
+    assert value_cache.shape == (nb, kvh, D, B)
+    assert block_tables.shape[0] == S and context_lens.shape == (S,)
+    out = np.zeros((S, H, D), np.float64)
+    _load().oracle_paged_attention_decode(
+        _ptr(out), _ptr(query_bits), _ptr(key_cache), _ptr(value_cache), _ptr(block_tables),
+        _ptr(context_lens), S, H, num_kv_heads, D, B, block_tables.shape[1], nb, float(scale),
+        float(k_scale), float(v_scale))
+    return out

@@ -660,3 +660,87 @@ void oracle_fp8_mqa_logits(const uint8_t *q, const uint8_t *k, const float *k_sc
         }
     }
 }
+
+/* ================================================================== */
+/* [P4] paged decode attention over fp8 pages (vLLM PR "[ROCm] Faster   */
+/* Custom Paged Attention kernels": the op schema paged_attention(out,  */
+/* exp_sums, max_logits, tmp_out, query, key_cache, value_cache,        */
+/* num_kv_heads, scale, block_tables, context_lens, block_size, ...,    */
+/* kv_cache_dtype, k_scale, v_scale, ..., partition_size)).             */
+/* ================================================================== */
+
+/* One decode query per sequence.  For sequence s and head h (kv head     */
+/* kvh = h / (num_heads / num_kv_heads)), token t < context_lens[s] lives */
+/* in page block_tables[s][t / B] at offset t % B; its key and value are  */
+/*   k_t[d] = E4M3dec(key_cache[page][kvh][d/16][t%B][d%16]) * k_scale     */
+/*   v_t[d] = E4M3dec(value_cache[page][kvh][d][t%B]) * v_scale           */
+/* and out[s][h] = sum_t softmax_t(scale * q.k_t) * v_t, in binary64.     */
+/* Tokens whose page id is outside [0, num_blocks) or whose block-table   */
+/* column is >= max_blocks are left out of the softmax; a sequence with   */
+/* no token left gets a zero row.  q is bf16 (widened exactly).           */
+void oracle_paged_attention_decode(double *out, const uint16_t *query,
+                                   const uint8_t *key_cache, const uint8_t *value_cache,
+                                   const int32_t *block_tables, const int32_t *context_lens,
+                                   int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_size, int32_t block_size, int32_t max_blocks,
+                                   int64_t num_blocks, double scale, float k_scale, float v_scale)
+{
+    const int32_t group = num_heads / num_kv_heads;
+    int32_t s, h;
+    for (s = 0; s < num_seqs; ++s) {
+        const int64_t L = context_lens[s];
+        for (h = 0; h < num_heads; ++h) {
+            const int32_t kvh = h / group;
+            const uint16_t *q = query + ((int64_t)s * num_heads + h) * head_size;
+            double *o = out + ((int64_t)s * num_heads + h) * head_size;
+            double m = -INFINITY, denom = 0.0;
+            int64_t t;
+            int32_t d;
+            for (d = 0; d < head_size; ++d)
+                o[d] = 0.0;
+            /* pass 1: the largest logit */
+            for (t = 0; t < L; ++t) {
+                int64_t j = t / block_size, page;
+                double dot = 0.0, logit;
+                if (j >= max_blocks) continue;
+                page = block_tables[(int64_t)s * max_blocks + j];
+                if (page < 0 || page >= num_blocks) continue;
+                for (d = 0; d < head_size; ++d) {
+                    const uint8_t c = key_cache[(((page * num_kv_heads + kvh) * (head_size / 16) +
+                                                  d / 16) * block_size + t % block_size) * 16 +
+                                                d % 16];
+                    dot += (double)oracle_bf16_to_f32(q[d]) *
+                           ((double)oracle_e4m3_decode(c) * (double)k_scale);
+                }
+                logit = scale * dot;
+                if (logit > m) m = logit;
+            }
+            if (m == -INFINITY)
+                continue;           /* no token: zero row */
+            /* pass 2: weights and the weighted sum of values */
+            for (t = 0; t < L; ++t) {
+                int64_t j = t / block_size, page;
+                double dot = 0.0, w;
+                if (j >= max_blocks) continue;
+                page = block_tables[(int64_t)s * max_blocks + j];
+                if (page < 0 || page >= num_blocks) continue;
+                for (d = 0; d < head_size; ++d) {
+                    const uint8_t c = key_cache[(((page * num_kv_heads + kvh) * (head_size / 16) +
+                                                  d / 16) * block_size + t % block_size) * 16 +
+                                                d % 16];
+                    dot += (double)oracle_bf16_to_f32(q[d]) *
+                           ((double)oracle_e4m3_decode(c) * (double)k_scale);
+                }
+                w = exp(scale * dot - m);
+                denom += w;
+                for (d = 0; d < head_size; ++d) {
+                    const uint8_t c = value_cache[((page * num_kv_heads + kvh) * head_size + d) *
+                                                  block_size + t % block_size];
+                    o[d] += w * ((double)oracle_e4m3_decode(c) * (double)v_scale);
+                }
+            }
+            for (d = 0; d < head_size; ++d)
+                o[d] /= denom;
+        }
+    }
+}

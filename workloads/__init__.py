@@ -335,3 +335,41 @@ def mqa_logits_case(seed, num_q, num_heads, num_k, causal_lens=None, head_dim=12
     k_scale = g.uniform(0.001, 0.01, size=num_k).astype(np.float32)
     weights = (normal_f32(g, (num_q, num_heads)) / np.float32(8)).astype(np.float32)
     return MqaLogitsCase(q, k, k_scale, weights, ks, ke)
+
+
+@dataclass
+class PagedAttentionCase:
+    """Decode attention over fp8 KV pages in vLLM's layouts."""
+    query: np.ndarray          # uint16 bf16 patterns [S, H, D]
+    key_cache: np.ndarray      # uint8 E4M3 codes [num_blocks, KVH, D/16, B, 16]
+    value_cache: np.ndarray    # uint8 E4M3 codes [num_blocks, KVH, D, B]
+    block_tables: np.ndarray   # int32 [S, maxb]
+    context_lens: np.ndarray   # int32 [S]
+    num_kv_heads: int
+    scale: float
+    k_scale: float
+    v_scale: float
+
+
+def paged_attention_case(seed, num_seqs, num_heads, num_kv_heads, block_size=16, head_size=128,
+                         max_context=2048, min_context=1, lens=None, spare_pages=3):
+    """Context lengths uniform in [min_context, max_context] (or `lens`); each
+    sequence owns whole pages from one seeded shuffle.  Cache codes are the
+    E4M3 codes of N(0,1)*32 (torch's cast), queries N(0,1) in bf16, scale
+    1/sqrt(head_size), k_scale and v_scale uniform in [0.02, 0.05] (the size
+    amax/448 has for unit-normal K and V)."""
+    g = rng(seed)
+    if lens is None:
+        lens = g.integers(min_context, max_context + 1, size=num_seqs)
+    lens = [int(n) for n in lens]
+    need = [-(-n // block_size) for n in lens]
+    num_blocks = sum(need) + spare_pages
+    table, _ = _pages_table(g, lens, block_size, num_blocks)
+    D = head_size
+    q = bf16_bits(normal_f32(g, (num_seqs, num_heads, D)))
+    kc = _e4m3_codes(normal_f32(g, (num_blocks, num_kv_heads, D // 16, block_size, 16)) *
+                     np.float32(32))
+    vc = _e4m3_codes(normal_f32(g, (num_blocks, num_kv_heads, D, block_size)) * np.float32(32))
+    k_scale, v_scale = (float(np.float32(x)) for x in g.uniform(0.02, 0.05, size=2))
+    return PagedAttentionCase(q, kc, vc, table.astype(np.int32), np.array(lens, np.int32),
+                              num_kv_heads, float(np.float32(1.0 / np.sqrt(D))), k_scale, v_scale)
