@@ -41,6 +41,13 @@
  *   pkv_fp8_mqa_logits        indexer scores of query tokens against the
  *                             gathered keys (fp8 MFMA contraction).
  *
+ * and the decode consumer of fp8 K/V pages with per-tensor scales:
+ *
+ *   pkv_paged_attention_decode  one query token per sequence attends over
+ *                             its paged fp8 keys and values (vLLM PR
+ *                             "[ROCm] Faster Custom Paged Attention
+ *                             kernels").
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every buffer pointer is a DEVICE pointer owned by the caller.  The
@@ -87,7 +94,7 @@ extern "C" {
 #define PKV_DTYPE_F16 1
 
 /* ABI version of this header; bumped when a signature changes. */
-#define PKV_ABI_VERSION 4
+#define PKV_ABI_VERSION 5
 int pkv_abi_version(void);
 
 /* Message for the last non-zero status on this thread ("" if none). */
@@ -303,6 +310,63 @@ int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void *k,
                        const int32_t *ke, float *logits, int64_t row_stride, int64_t row_cols,
                        int32_t num_q, int32_t num_heads, int64_t num_k, int32_t head_dim,
                        void *stream);
+
+/*
+ * Paged decode attention over fp8 pages (vLLM PR "[ROCm] Faster Custom Paged
+ * Attention kernels": the op paged_attention(out, exp_sums, max_logits,
+ * tmp_out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
+ * context_lens, block_size, max_context_len, ..., kv_cache_dtype, k_scale,
+ * v_scale, ..., partition_size), with an fp8 cache and per-tensor scales).
+ *
+ * For sequence s < num_seqs and head h < num_heads, with
+ * kvh = h / (num_heads / num_kv_heads) and tokens t < context_lens[s]:
+ *     k_t[d] = E4M3dec(key_cache[page][kvh][d/16][t%B][d%16]) * k_scale
+ *     v_t[d] = E4M3dec(value_cache[page][kvh][d][t%B]) * v_scale
+ *     page   = block_tables[s*max_blocks_per_seq + t/B]
+ *     out[s][h][:] = bf16( sum_t softmax_t(scale * q[s][h] . k_t) v_t )
+ * Tokens whose page id is outside [0, num_blocks) are left out of the
+ * softmax; a sequence with no token left (or context_lens[s] <= 0) gets a
+ * zero row.  Only tokens t < ceil(max_context_len / partition_size) *
+ * partition_size are read: max_context_len must be >= every context_lens[s].
+ *
+ * The work is split, as on the page, into partitions of partition_size
+ * tokens: a first kernel writes each partition's softmax denominator,
+ * maximum logit and normalised partial output to the caller's workspace,
+ * and a second combines them.  The dot products run on bf16 MFMA
+ * (v_mfma_f32_16x16x32_bf16; fp8 keys and values are exact in bf16, the
+ * probabilities enter as a bf16 high + low pair) with binary32
+ * accumulation, and the exponentials on the hardware exp2; results agree
+ * with the exact value within a bound (the tests state it), not bit for bit.
+ *
+ *   out          bf16 [num_seqs, num_heads, head_size]; 16-byte aligned.
+ *   exp_sums,    binary32 [num_seqs, num_heads, max_num_partitions] with
+ *   max_logits   max_num_partitions = ceil(max_context_len/partition_size);
+ *                workspace written and read by the call.
+ *   tmp_out      binary32 [num_seqs, num_heads, max_num_partitions,
+ *                head_size]; workspace.  16-byte aligned.
+ *   query        bf16 [num_seqs, num_heads, head_size]; 16-byte aligned.
+ *   key_cache    E4M3 [num_blocks, num_kv_heads, head_size/16, block_size,
+ *                16]; 16-byte aligned.
+ *   value_cache  E4M3 [num_blocks, num_kv_heads, head_size, block_size];
+ *                16-byte aligned.
+ *   block_tables int32 [num_seqs, max_blocks_per_seq].
+ *   context_lens int32 [num_seqs].
+ *   head_size 128; block_size a positive multiple of 16;
+ *   num_heads a multiple of num_kv_heads with at most 16 query heads per KV
+ *   head; partition_size 32, 64, 128 or 256; scale, k_scale, v_scale finite
+ *   host values (k_scale, v_scale > 0).
+ * The workspace is the caller's: the library allocates nothing.  Calls that
+ * share a workspace must be ordered on one stream.
+ */
+int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_logits, float *tmp_out,
+                               const void *query, const void *key_cache,
+                               const void *value_cache, const int32_t *block_tables,
+                               const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t max_context_len,
+                               int64_t num_blocks, float scale, float k_scale, float v_scale,
+                               int32_t partition_size, void *stream);
+
 
 /*
  * Diagnostics: the device codecs the store kernels use, exposed so that a

@@ -81,10 +81,13 @@ def _load():
     lib.pkv_diag_narrow.argtypes = [P, P, i64, i32, P]
     lib.pkv_fp8_mqa_logits.argtypes = [P, i64, P, P, P, P, P, P, i64, i64, i32, i32, i64, i32, P]
     lib.pkv_diag_encode_e2m1.argtypes = [P, P, i64, P]
+    f32 = ctypes.c_float
+    lib.pkv_paged_attention_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
+                                               i32, i32, i64, f32, f32, f32, i32, P]
     for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
                  "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
                  "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "pkv_diag_narrow",
-                 "pkv_fp8_mqa_logits"):
+                 "pkv_fp8_mqa_logits", "pkv_paged_attention_decode"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -420,3 +423,80 @@ def pkv_fp8_mqa_logits(q, k, k_scale, weights, ks, ke, logits, stream=None):
         q.data_ptr(), q.stride(0) * q.element_size(), k.data_ptr(), k_scale.data_ptr(),
         weights.data_ptr(), ks.data_ptr(), ke.data_ptr(), logits.data_ptr(), logits.stride(0),
         logits.shape[1], num_q, num_heads, num_k, head_dim, _stream(stream)))
+
+
+def paged_attention_workspace(num_seqs: int, num_heads: int, max_context_len: int,
+                              partition_size: int = 256, head_size: int = 128, device="cuda"):
+    """The caller-owned workspace of pkv_paged_attention_decode: exp_sums and
+    max_logits float32 [S, H, P], tmp_out float32 [S, H, P, head_size], with
+    P = ceil(max_context_len / partition_size) (at least 1)."""
+    parts = max(1, -(-int(max_context_len) // int(partition_size)))
+    exp_sums = torch.empty((num_seqs, num_heads, parts), dtype=torch.float32, device=device)
+    max_logits = torch.empty_like(exp_sums)
+    tmp_out = torch.empty((num_seqs, num_heads, parts, head_size), dtype=torch.float32,
+                          device=device)
+    return exp_sums, max_logits, tmp_out
+
+
+def pkv_paged_attention_decode(out, exp_sums, max_logits, tmp_out, query, key_cache,
+                               value_cache, num_kv_heads: int, scale: float, block_tables,
+                               context_lens, block_size: int, max_context_len: int,
+                               k_scale: float = 1.0, v_scale: float = 1.0,
+                               partition_size: int = 256, stream=None):
+    """Decode attention over fp8 KV pages with per-tensor scales.
+
+    out:          bfloat16 [num_seqs, num_heads, 128], contiguous.
+    exp_sums, max_logits: float32 [num_seqs, num_heads, P] workspace,
+                  tmp_out float32 [num_seqs, num_heads, P, 128], with
+                  P = ceil(max_context_len / partition_size)
+                  (paged_attention_workspace makes them).
+    query:        bfloat16 [num_seqs, num_heads, 128], contiguous.
+    key_cache:    uint8 / float8_e4m3fn [num_blocks, num_kv_heads, 8, block_size, 16].
+    value_cache:  uint8 / float8_e4m3fn [num_blocks, num_kv_heads, 128, block_size].
+    block_tables: int32 [num_seqs, max_blocks_per_seq]; context_lens int32 [num_seqs].
+    scale, k_scale, v_scale: host floats.
+    """
+    _dev(out, "out", torch.bfloat16)
+    _dev(query, "query", torch.bfloat16)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        _dev(t, n)
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must be uint8 or float8_e4m3fn")
+    for t, n in ((exp_sums, "exp_sums"), (max_logits, "max_logits"), (tmp_out, "tmp_out")):
+        _dev(t, n, torch.float32)
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (exp_sums, "exp_sums"),
+                 (max_logits, "max_logits"), (tmp_out, "tmp_out"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens")):
+        _contig(t, n)
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_heads, head_size]")
+    num_seqs, num_heads, head_size = query.shape
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the shape of query")
+    if key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise ValueError("key_cache must be [nb, KVH, D/16, B, 16] and value_cache [nb, KVH, D, B]")
+    num_blocks = key_cache.shape[0]
+    if (tuple(key_cache.shape) != (num_blocks, num_kv_heads, head_size // 16, block_size, 16) or
+            tuple(value_cache.shape) != (num_blocks, num_kv_heads, head_size, block_size)):
+        raise ValueError("key_cache / value_cache shapes do not match num_kv_heads, head_size "
+                         "and block_size")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if context_lens.numel() != num_seqs:
+        raise ValueError("context_lens must have num_seqs entries")
+    parts = -(-int(max_context_len) // int(partition_size)) if partition_size > 0 else 0
+    if exp_sums.dim() != 3 or tuple(exp_sums.shape[:2]) != (num_seqs, num_heads) or \
+            tuple(max_logits.shape) != tuple(exp_sums.shape) or \
+            tuple(tmp_out.shape) != (*exp_sums.shape, head_size):
+        raise ValueError("workspace shapes do not match [num_seqs, num_heads, P(, head_size)]")
+    if exp_sums.shape[2] != max(parts, 1) and exp_sums.shape[2] != parts:
+        raise ValueError(f"workspace holds {exp_sums.shape[2]} partitions, the call needs {parts}")
+    _check(_lib.pkv_paged_attention_decode(
+        out.data_ptr(), exp_sums.data_ptr(), max_logits.data_ptr(), tmp_out.data_ptr(),
+        query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(), block_tables.data_ptr(),
+        context_lens.data_ptr(), num_seqs, num_heads, num_kv_heads, head_size, block_size,
+        block_tables.shape[1], max_context_len, num_blocks, scale, k_scale, v_scale,
+        partition_size, _stream(stream)))

@@ -27,6 +27,7 @@ SOURCES = [
     "store_kv_fp4.hip",
     "gather_dequant.hip",
     "mqa_logits.hip",
+    "paged_attention.hip",
     "diag_codecs.hip",
 ]
 

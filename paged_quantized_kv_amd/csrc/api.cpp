@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -311,6 +312,63 @@ int pkv_fp8_mqa_logits(const void* q, int64_t q_token_stride, const void* k, con
                        static_cast<const uint8_t*>(k), k_scale, weights, ks, ke, logits,
                        row_stride, row_cols, num_q, num_heads, num_k};
   return launched(pkv::launch_fp8_mqa_logits(a, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, float* tmp_out,
+                               const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int64_t num_blocks, float scale,
+                               float k_scale, float v_scale, int32_t partition_size,
+                               void* stream) {
+  static const char* op = "pkv_paged_attention_decode";
+  if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs must be >= 0, got %d", op, num_seqs);
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(PKV_EINVAL, "%s: num_heads and num_kv_heads must be > 0, got %d and %d", op,
+                num_heads, num_kv_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PKV_EINVAL, "%s: num_heads %d is not a multiple of num_kv_heads %d", op,
+                num_heads, num_kv_heads);
+  if (num_heads / num_kv_heads > 16)
+    return fail(PKV_EUNSUPPORTED, "%s: at most 16 query heads per KV head, got %d", op,
+                num_heads / num_kv_heads);
+  if (head_size != 128) return fail(PKV_EUNSUPPORTED, "%s: head_size must be 128, got %d", op, head_size);
+  if (block_size <= 0 || block_size % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size must be a positive multiple of 16, got %d", op,
+                block_size);
+  if (partition_size != 32 && partition_size != 64 && partition_size != 128 && partition_size != 256)
+    return fail(PKV_EUNSUPPORTED, "%s: partition_size must be 32, 64, 128 or 256, got %d", op,
+                partition_size);
+  if (max_blocks_per_seq < 0)
+    return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be >= 0, got %d", op, max_blocks_per_seq);
+  if (max_context_len < 0)
+    return fail(PKV_EINVAL, "%s: max_context_len must be >= 0, got %d", op, max_context_len);
+  if (num_blocks <= 0) return fail(PKV_EINVAL, "%s: num_blocks must be > 0, got %lld", op, (long long)num_blocks);
+  if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
+    return fail(PKV_EINVAL, "%s: scale, k_scale and v_scale must be finite", op);
+  const int64_t parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+  if ((int64_t)num_seqs * num_heads * (parts > 0 ? parts : 1) * head_size > ((int64_t)1 << 40))
+    return fail(PKV_EUNSUPPORTED, "%s: workspace too large", op);
+  if ((int64_t)num_seqs * max_blocks_per_seq > INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: num_seqs * max_blocks_per_seq exceeds 2^31-1", op);
+  if (num_seqs == 0) return ok();
+  if (!out || !query || !context_lens || (max_context_len > 0 &&
+      (!exp_sums || !max_logits || !tmp_out || !key_cache || !value_cache || !block_tables)))
+    return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(tmp_out, 16) || !aligned(key_cache, 16) ||
+      !aligned(value_cache, 16))
+    return fail(PKV_EALIGN, "%s: out, query, tmp_out, key_cache and value_cache must be 16-byte aligned", op);
+  if (!aligned(exp_sums, 4) || !aligned(max_logits, 4) || !aligned(block_tables, 4) ||
+      !aligned(context_lens, 4))
+    return fail(PKV_EALIGN, "%s: exp_sums, max_logits, block_tables and context_lens must be 4-byte aligned", op);
+  pkv::PagedAttentionArgs a{static_cast<uint16_t*>(out), exp_sums, max_logits, tmp_out,
+                            static_cast<const uint16_t*>(query),
+                            static_cast<const uint8_t*>(key_cache),
+                            static_cast<const uint8_t*>(value_cache), block_tables, context_lens,
+                            num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                            max_context_len, num_blocks, scale, k_scale, v_scale, partition_size};
+  return launched(pkv::launch_paged_attention_decode(a, static_cast<hipStream_t>(stream)), op);
 }
 
 static int check_diag(const char* op, const float* y, const uint8_t* out, int64_t n) {

@@ -124,10 +124,34 @@ struct MqaLogitsArgs {
   int64_t num_k;
 };
 
+struct PagedAttentionArgs {
+  uint16_t* out;
+  float* exp_sums;
+  float* max_logits;
+  float* tmp_out;
+  const uint16_t* query;
+  const uint8_t* key_cache;
+  const uint8_t* value_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;
+  int64_t num_blocks;
+  float scale;
+  float k_scale;
+  float v_scale;
+  int32_t partition_size;
+};
+
 int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream);
 int launch_fp8_mqa_logits(const MqaLogitsArgs& a, hipStream_t stream);
 int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stream);
 int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream);
+int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t stream);
 int launch_store_indexer_k_fp8(const StoreFp8Args& a, hipStream_t stream);
 int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream);
 int launch_diag_e4m3(const float* y, uint8_t* out, int64_t n, hipStream_t stream);

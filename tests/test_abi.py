@@ -26,7 +26,8 @@ def test_header_declares_the_boundary():
     syms = declared_symbols()
     for s in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
               "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
-              "pkv_fp8_mqa_logits", "pkv_last_error", "pkv_abi_version"):
+              "pkv_fp8_mqa_logits", "pkv_paged_attention_decode", "pkv_last_error",
+              "pkv_abi_version"):
         assert s in syms
 
 
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
     for s in declared_symbols():
         assert s in exported, s
         assert getattr(lib, s) is not None
-    assert pkv.abi_version() == 4
+    assert pkv.abi_version() == 5
 
 
 def lib():
@@ -236,6 +237,47 @@ def test_mqa_logits_validation(kw, code, msg):
 def test_mqa_logits_empty_is_ok():
     assert lg(M=0, q=0, k=0, kscale=0, w=0, ks=0, ke=0, out=0) == PKV_OK
     assert lg(N=0, q=0, k=0, kscale=0, w=0, ks=0, ke=0, out=0) == PKV_OK
+
+
+def pa(**kw):
+    a = dict(out=A, es=A, ml=A, tmp=A, q=A, kc=A, vc=A, bt=A, cl=A, S=4, H=64, KVH=8, D=128,
+             B=16, maxb=8, maxc=128, nb=64, scale=0.088, ksc=0.03, vsc=0.04, P=256)
+    a.update(kw)
+    return lib().pkv_paged_attention_decode(a["out"], a["es"], a["ml"], a["tmp"], a["q"], a["kc"],
+                                            a["vc"], a["bt"], a["cl"], a["S"], a["H"], a["KVH"],
+                                            a["D"], a["B"], a["maxb"], a["maxc"], a["nb"],
+                                            a["scale"], a["ksc"], a["vsc"], a["P"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(S=-1), PKV_EINVAL, "num_seqs"),
+    (dict(KVH=0), PKV_EINVAL, "num_kv_heads"),
+    (dict(H=60), PKV_EINVAL, "not a multiple"),
+    (dict(H=136, KVH=8), PKV_EUNSUPPORTED, "at most 16"),
+    (dict(D=64), PKV_EUNSUPPORTED, "head_size must be 128"),
+    (dict(B=8), PKV_EUNSUPPORTED, "multiple of 16"),
+    (dict(B=0), PKV_EUNSUPPORTED, "multiple of 16"),
+    (dict(P=16), PKV_EUNSUPPORTED, "partition_size"),
+    (dict(P=512), PKV_EUNSUPPORTED, "partition_size"),
+    (dict(maxb=-1), PKV_EINVAL, "max_blocks_per_seq"),
+    (dict(maxc=-1), PKV_EINVAL, "max_context_len"),
+    (dict(nb=0), PKV_EINVAL, "num_blocks"),
+    (dict(scale=float("inf")), PKV_EINVAL, "finite"),
+    (dict(vsc=float("nan")), PKV_EINVAL, "finite"),
+    (dict(tmp=0), PKV_EINVAL, "null"),
+    (dict(out=0), PKV_EINVAL, "null"),
+    (dict(kc=A + 8), PKV_EALIGN, "16-byte"),
+    (dict(tmp=A + 4), PKV_EALIGN, "16-byte"),
+    (dict(es=A + 2), PKV_EALIGN, "4-byte"),
+    (dict(bt=A + 1), PKV_EALIGN, "4-byte"),
+])
+def test_paged_attention_validation(kw, code, msg):
+    assert pa(**kw) == code
+    assert msg in last_error()
+
+
+def test_paged_attention_empty_is_ok():
+    assert pa(S=0, out=0, es=0, ml=0, tmp=0, q=0, kc=0, vc=0, bt=0, cl=0) == PKV_OK
 
 
 def test_diag_validation():

@@ -1,0 +1,139 @@
+"""GPU parity of paged decode attention (pkv_paged_attention_decode) against
+the binary64 oracle on the same seeded inputs, within the per-element bound
+that attention_bound derives from the kernels' arithmetic.  Rows without a
+valid token must be exactly zero; page bytes past a context's end (here NaN
+codes) must not reach the result."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from attention_bound import attention_bound
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import paged_quantized_kv_amd as pkv
+
+DEV = "cuda:0"
+
+
+def banner(name):
+    print(f"\n[case] {name}", flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run(c, partition_size=256, max_context_len=None, stream=None, ws=None):
+    S, H, D = c.query.shape
+    B = c.key_cache.shape[3]
+    maxc = int(c.context_lens.max(initial=0)) if max_context_len is None else max_context_len
+    q = dev(c.query.view(np.int16)).view(torch.bfloat16)
+    out = torch.full((S, H, D), float("nan"), dtype=torch.bfloat16, device=DEV)
+    if ws is None:
+        ws = pkv.paged_attention_workspace(S, H, maxc, partition_size, device=DEV)
+    pkv.pkv_paged_attention_decode(out, *ws, q, dev(c.key_cache), dev(c.value_cache),
+                                   c.num_kv_heads, c.scale, dev(c.block_tables),
+                                   dev(c.context_lens), B, maxc, c.k_scale, c.v_scale,
+                                   partition_size=partition_size, stream=stream)
+    torch.cuda.synchronize()
+    return out.to(torch.float64).cpu().numpy()
+
+
+def reference(c, rows=None):
+    sel = np.arange(c.query.shape[0]) if rows is None else np.asarray(rows)
+    ref = oracle.paged_attention_decode(
+        np.ascontiguousarray(c.query[sel]), c.key_cache, c.value_cache,
+        np.ascontiguousarray(c.block_tables[sel]), np.ascontiguousarray(c.context_lens[sel]),
+        c.num_kv_heads, c.scale, c.k_scale, c.v_scale)
+    b = attention_bound(c.query, c.key_cache, c.value_cache, c.block_tables, c.context_lens,
+                        c.num_kv_heads, c.scale, c.k_scale, c.v_scale, rows=sel)
+    return ref, b
+
+
+def check(got, ref, b):
+    assert not np.isnan(got).any(), "NaN in the output"
+    err = np.abs(got - ref)
+    worst = float(np.max(err / np.maximum(b, 1e-300))) if err.size else 0.0
+    zero = b == 0
+    assert np.all(got[zero] == 0), "rows without a valid token must be zero"
+    assert np.all(err <= b), f"max err/bound = {worst:.3g}"
+    return worst
+
+
+@pytest.mark.parametrize("H,KVH,B,P", [
+    (8, 1, 16, 256),     # 8 query heads per KV head
+    (32, 2, 16, 64),     # 16 per KV head (the largest group)
+    (4, 4, 32, 32),      # no grouping, 32-token pages, smallest partition
+    (14, 2, 16, 128),    # a group of 7
+    (64, 8, 16, 256),    # Llama-3.1-70B heads
+    (16, 1, 64, 256),    # 64-token pages
+])
+def test_shapes(H, KVH, B, P):
+    banner(f"paged attention H={H} KVH={KVH} B={B} P={P}")
+    lens = [1, 15, 16, 17, 31, 255, 256, 257, 600, 1029]
+    c = workloads.paged_attention_case(40 + H + B + P, len(lens), H, KVH, block_size=B, lens=lens)
+    ref, b = reference(c)
+    worst = check(run(c, P), ref, b)
+    print(f"max err / bound = {worst:.3g}", flush=True)
+
+
+def test_long_contexts_many_partitions():
+    banner("paged attention long contexts, P=32")
+    lens = [4100, 3000, 2049]
+    c = workloads.paged_attention_case(9, len(lens), 16, 2, lens=lens)
+    ref, b = reference(c)
+    check(run(c, 32), ref, b)
+    check(run(c, 256), ref, b)
+
+
+def test_edges_empty_invalid_pages_and_stale_bytes():
+    """Context 0; a sequence whose only pages are invalid ids (-1 and
+    >= num_blocks); invalid pages in the middle of a context; a context that
+    ends inside a page whose later slots hold NaN codes; max_context_len
+    larger than every context."""
+    banner("paged attention edges")
+    lens = [0, 40, 300, 77, 1]
+    c = workloads.paged_attention_case(21, len(lens), 8, 2, lens=lens)
+    nb = c.key_cache.shape[0]
+    c.block_tables[1, :3] = [-1, nb, nb + 7]            # no valid page at all
+    c.block_tables[2, 3] = -5                           # a hole in the middle
+    c.block_tables[2, 7] = nb + 1
+    p = c.block_tables[3, 77 // 16]                     # the page where seq 3 ends
+    c.key_cache[p, :, :, 77 % 16:, :] = 0x7F            # NaN codes past the end
+    c.value_cache[p, :, :, 77 % 16:] = 0xFF
+    ref, b = reference(c)
+    assert np.all(ref[0] == 0) and np.all(ref[1] == 0)
+    check(run(c, 256), ref, b)
+    check(run(c, 64, max_context_len=1000), ref, b)
+
+
+def test_repeated_calls_share_a_workspace_on_a_side_stream():
+    banner("paged attention workspace reuse, side stream")
+    c1 = workloads.paged_attention_case(31, 6, 64, 8, lens=[900, 1, 513, 64, 2000, 100])
+    c2 = workloads.paged_attention_case(32, 6, 64, 8, lens=[5, 1999, 17, 256, 1, 700])
+    ws = pkv.paged_attention_workspace(6, 64, 2000, 256, device=DEV)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        g1 = run(c1, 256, max_context_len=2000, stream=s, ws=ws)
+        g2 = run(c2, 256, max_context_len=2000, stream=s, ws=ws)
+    check(g1, *reference(c1))
+    check(g2, *reference(c2))
+
+
+def test_decode_batch_sampled():
+    """The decode batch at its full size, in the launch configuration that is
+    timed (200 sequences, Llama-3.1-70B heads, 16-token pages, partitions of
+    256); the oracle checks a sample of sequences that includes the longest
+    and the shortest."""
+    banner("paged attention decode batch, sampled rows")
+    c = workloads.decode_batch()
+    got = run(c, 256)
+    L = c.context_lens
+    rows = sorted({int(np.argmax(L)), int(np.argmin(L)), *range(0, len(L), 23)})
+    ref, b = reference(c, rows)
+    worst = check(got[rows], ref, b)
+    print(f"rows {rows}: max err / bound = {worst:.3g}", flush=True)

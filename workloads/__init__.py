@@ -307,7 +307,7 @@ class MqaLogitsCase:
 def _e4m3_codes(x: np.ndarray) -> np.ndarray:
     """Codes of float32 values already inside the E4M3 range (torch's cast)."""
     import torch
-    t = torch.from_numpy(np.clip(x, -448, 448).astype(np.float32))
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).clamp(-448, 448)
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
@@ -367,9 +367,28 @@ def paged_attention_case(seed, num_seqs, num_heads, num_kv_heads, block_size=16,
     table, _ = _pages_table(g, lens, block_size, num_blocks)
     D = head_size
     q = bf16_bits(normal_f32(g, (num_seqs, num_heads, D)))
-    kc = _e4m3_codes(normal_f32(g, (num_blocks, num_kv_heads, D // 16, block_size, 16)) *
-                     np.float32(32))
-    vc = _e4m3_codes(normal_f32(g, (num_blocks, num_kv_heads, D, block_size)) * np.float32(32))
+    kc = normal_f32(g, (num_blocks, num_kv_heads, D // 16, block_size, 16))
+    kc *= np.float32(32)
+    kc = _e4m3_codes(kc)
+    vc = normal_f32(g, (num_blocks, num_kv_heads, D, block_size))
+    vc *= np.float32(32)
+    vc = _e4m3_codes(vc)
     k_scale, v_scale = (float(np.float32(x)) for x in g.uniform(0.02, 0.05, size=2))
     return PagedAttentionCase(q, kc, vc, table.astype(np.int32), np.array(lens, np.int32),
                               num_kv_heads, float(np.float32(1.0 / np.sqrt(D))), k_scale, v_scale)
+
+
+DECODE_SEQS = 200
+DECODE_HEADS, DECODE_KV_HEADS, DECODE_HEAD_SIZE, DECODE_BLOCK = 64, 8, 128, 16
+DECODE_MIN_CONTEXT, DECODE_MAX_CONTEXT = 128, 2560
+
+
+def decode_batch(seed=2024):
+    """One decode step of the fp8-KV serving runs on the Custom Paged Attention
+    page: Llama-3.1-70B attention shapes (64 query heads, 8 KV heads, head
+    size 128), 16-token pages, 200 requests (the page's prompt count) whose
+    contexts are uniform in [128, 2560] (its 128- and 512-token inputs plus up
+    to 2048 generated tokens)."""
+    return paged_attention_case(seed, DECODE_SEQS, DECODE_HEADS, DECODE_KV_HEADS,
+                                block_size=DECODE_BLOCK, head_size=DECODE_HEAD_SIZE,
+                                max_context=DECODE_MAX_CONTEXT, min_context=DECODE_MIN_CONTEXT)
