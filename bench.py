@@ -26,6 +26,12 @@ of `value`): pkv_gather_indexer_k_dequant (indexer pages -> bf16 rows) and
 pkv_gather_kv_fp4_dequant (NVFP4 pages -> bf16 K and V rows), reported under
 `reader_side`.
 
+Then the decode consumer of fp8 KV pages is timed on its own batch (not
+part of `value` either): pkv_paged_attention_decode over one decode step of
+200 requests with Llama-3.1-70B attention shapes (64 query heads, 8 KV heads,
+head size 128, 16-token pages, contexts uniform in [128, 2560]: 0.5 GB of K/V
+codes), reported under `decode_attention`.
+
 Printed: one JSON line.  `value` = algorithmic bytes of one step / measured
 step time (GB/s); per-kernel durations come from HIP events recorded on the
 launch stream around each launch (timing-only events, without the cache
@@ -57,6 +63,7 @@ KERNEL_SOURCES = {
     "gather_indexer_k_fp8": ["gather_indexer_k_fp8.hip", "device_common.h"],
     "gather_indexer_k_dequant": ["gather_dequant.hip", "device_common.h"],
     "gather_kv_fp4_dequant": ["gather_dequant.hip", "device_common.h"],
+    "paged_attention_decode": ["paged_attention.hip", "device_common.h"],
 }
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -69,10 +76,10 @@ def source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def measured_traffic(kernel: str, workload: str = "prefill_256x1000"):
     """HBM bytes per launch from a committed counter summary, if it was taken
     on the current source of the kernel; else None."""
-    path = os.path.join(PROFILES, f"{kernel}_prefill_256x1000_pmc.md")
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -93,6 +100,8 @@ def parse_args():
                    help="skip the CPU oracle timing (profiling runs)")
     p.add_argument("--reader-steps", type=int, default=50,
                    help="timed iterations of the reader-side gathers (0: skip them)")
+    p.add_argument("--decode-steps", type=int, default=50,
+                   help="timed calls of the paged decode attention (0: skip them)")
     p.add_argument("--calibration-copy", action="store_true",
                    help="run a plain 256 MiB fp32 copy-like kernel (torch.neg) before the "
                         "timed steps, for scaling hardware byte counters")
@@ -232,6 +241,61 @@ def time_reader(args, pkv, torch, timing, stream, sets, w, f, bt, cu, c4, k4s, v
     return ms
 
 
+def decode_attention_bytes(c):
+    """Bytes decode attention must move: the K and V codes of every token of
+    every sequence (each read once), the bf16 queries and outputs, and the
+    block-table entries and context lengths it reads."""
+    S, H, D = c.query.shape
+    B = c.key_cache.shape[3]
+    L = c.context_lens.astype(int)
+    kv = int(L.sum()) * c.num_kv_heads * 2 * D
+    return kv + 2 * (S * H * D * 2) + 4 * int(sum(-(-n // B) for n in L)) + 4 * S
+
+
+def time_decode_attention(args, pkv, torch, timing, stream, workloads, np):
+    """Average duration (ms) of one pkv_paged_attention_decode call (partition
+    and reduce kernels) over the decode batch, timed like the step's kernels.
+    Its 0.5 GB of K/V codes is larger than the Infinity Cache, so each call
+    reads them from HBM."""
+    c = workloads.decode_batch()
+    S, H, D = c.query.shape
+    B = c.key_cache.shape[3]
+    maxc = int(c.context_lens.max())
+
+    def to(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    q = to(c.query.view(np.int16)).view(torch.bfloat16)
+    kc, vc, bt, cl = to(c.key_cache), to(c.value_cache), to(c.block_tables), to(c.context_lens)
+    out = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
+    ws = pkv.paged_attention_workspace(S, H, maxc, 256, device="cuda")
+
+    def call():
+        pkv.pkv_paged_attention_decode(out, *ws, q, kc, vc, c.num_kv_heads, c.scale, bt, cl, B,
+                                       maxc, c.k_scale, c.v_scale, partition_size=256)
+
+    evs = [[timing.create() for _ in range(2)] for _ in range(args.decode_steps)]
+    for _ in range(min(args.warmup, 20)):
+        call()
+    torch.cuda.synchronize()
+    for e in evs:
+        timing.record(e[0], stream)
+        call()
+        timing.record(e[1], stream)
+    torch.cuda.synchronize()
+    ms = sum(timing.elapsed_ms(e[0], e[1]) for e in evs) / args.decode_steps
+    timing.destroy_all()
+    nbytes = decode_attention_bytes(c)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"us": round(ms * 1e3, 2), "alg_bytes": nbytes, "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "seqs_per_s": round(S / (ms * 1e-3), 1),
+            "context_tokens": int(c.context_lens.sum()),
+            "workload": "decode step: 200 req, H=64, KVH=8, D=128, B=16, contexts U[128, 2560], "
+                        "fp8 E4M3 K/V, partitions of 256",
+            "traffic": measured_traffic("paged_attention_decode", "decode_200req")}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -347,6 +411,10 @@ def main():
                       "traffic": measured_traffic(n)}
                   for n in rb}
 
+    decode = None
+    if args.decode_steps > 0:
+        decode = time_decode_attention(args, pkv, torch, timing, stream, workloads, np)
+
     alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
     step_bytes = sum(alg.values())
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -393,6 +461,8 @@ def main():
     }
     if reader is not None:
         out["reader_side"] = reader
+    if decode is not None:
+        out["decode_attention"] = decode
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, f, step_bytes)
     print(json.dumps(out), flush=True)

@@ -337,8 +337,8 @@ int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, fl
   if (block_size <= 0 || block_size % 16 != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size must be a positive multiple of 16, got %d", op,
                 block_size);
-  if (partition_size != 32 && partition_size != 64 && partition_size != 128 && partition_size != 256)
-    return fail(PKV_EUNSUPPORTED, "%s: partition_size must be 32, 64, 128 or 256, got %d", op,
+  if (partition_size != 64 && partition_size != 128 && partition_size != 256 && partition_size != 512)
+    return fail(PKV_EUNSUPPORTED, "%s: partition_size must be 64, 128, 256 or 512, got %d", op,
                 partition_size);
   if (max_blocks_per_seq < 0)
     return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be >= 0, got %d", op, max_blocks_per_seq);
@@ -347,9 +347,11 @@ int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, fl
   if (num_blocks <= 0) return fail(PKV_EINVAL, "%s: num_blocks must be > 0, got %lld", op, (long long)num_blocks);
   if (!std::isfinite(scale) || !std::isfinite(k_scale) || !std::isfinite(v_scale))
     return fail(PKV_EINVAL, "%s: scale, k_scale and v_scale must be finite", op);
+  if (max_context_len > (1 << 30))
+    return fail(PKV_EUNSUPPORTED, "%s: max_context_len must be <= 2^30, got %d", op, max_context_len);
   const int64_t parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
-  if ((int64_t)num_seqs * num_heads * (parts > 0 ? parts : 1) * head_size > ((int64_t)1 << 40))
-    return fail(PKV_EUNSUPPORTED, "%s: workspace too large", op);
+  if ((int64_t)num_seqs * num_heads >= INT32_MAX || (int64_t)num_seqs * num_kv_heads * parts >= INT32_MAX)
+    return fail(PKV_EUNSUPPORTED, "%s: num_seqs * num_heads and the partition count must stay below 2^31", op);
   if ((int64_t)num_seqs * max_blocks_per_seq > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "%s: num_seqs * max_blocks_per_seq exceeds 2^31-1", op);
   if (num_seqs == 0) return ok();

@@ -11,18 +11,25 @@
 //   v_t = E4M3dec(value_cache[page][kvh][d][t%B]) * v_scale,
 //   page = block_tables[s][t/B], kvh = h / (num_heads / num_kv_heads).
 //
-// Partition kernel: one wave per (sequence, kv head, partition of
-// partition_size tokens); no LDS is shared between waves and there is no
-// barrier.  The wave's G = num_heads/num_kv_heads query heads are the 16 rows
-// of v_mfma_f32_16x16x32_bf16 operands (rows >= G are zero); fp8 keys and
-// values become bf16 exactly (4 significant bits fit in 8).  Per 16-token
-// tile (one page, block_size a multiple of 16): 4 MFMAs give the 16 x 16
-// logits.  After the partition's max and exp-sum per head, the probabilities
-// go through a wave-private LDS slice (transposed to operand order) as bf16
-// hi + lo parts (16 significant bits), and 2 x 8 MFMAs per 32 tokens give
-// the 16 x 128 partial output.  The partition writes its normalised partial
-// output, exp-sum and max to the caller's workspace (exp_sums, max_logits,
-// tmp_out), as the page's schema does.
+// Partition kernel: one workgroup per (sequence, kv head, partition of
+// partition_size tokens), partition_size / 64 waves of 64 tokens each.  The
+// G = num_heads/num_kv_heads query heads of the kv head are the 16 rows of
+// v_mfma_f32_16x16x32_bf16 operands (rows >= G are zero); fp8 keys and values
+// become bf16 exactly (4 significant bits fit in 8).  A wave first issues
+// every load it needs -- two 16-byte key rows and eight 16-byte value rows
+// per lane, 16 KB per wave -- so that its whole share of the pages is in
+// flight at once, then computes.  The contractions run in the order those
+// loads deliver: over d, chunk c takes d = 16 (grp + 4 (c/2)) + 8 (c%2) + e
+// (the query operand is loaded in the same order); over tokens, the k index
+// 8 grp + e of MFMA h is token 16 grp + 8 h + e.  Per 16-token tile (inside
+// one page: block_size is a multiple of 16) 4 MFMAs give the 16 x 16 logits;
+// after the wave's max and exp-sum per head, the probabilities go through a
+// wave-private LDS slice (to operand order) as a bf16 high part plus the bf16
+// of the exact remainder (16 significant bits), and 4 MFMAs per 16 values of
+// d give the 16 x 128 partial output.  The waves then meet in LDS: common
+// maximum, rescaled exp-sums, summed outputs; the workgroup writes the
+// partition's normalised output, exp-sum and maximum to the caller's
+// workspace (exp_sums, max_logits, tmp_out), as the page's schema does.
 //
 // Reduce kernel: one wave per (sequence, head) combines the partitions:
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
@@ -44,8 +51,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kPaThreads = 256;
 constexpr int kPaWaves = kPaThreads / kWave;
 constexpr int kPaD = 128;        // head_size
-constexpr int kPaMaxPart = 256;  // largest partition_size (logit registers)
-constexpr int kPaChunk = 32;     // tokens per PV step (one MFMA K)
+constexpr int kPaWaveTokens = 64;  // tokens per wave in the partition kernel
+constexpr int kPaTiles = kPaWaveTokens / 16;
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf a, const v8bf b, const v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -86,90 +93,143 @@ __device__ __forceinline__ uint16_t bf16_rn(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <int kTiles>  // partition_size / 16
-__global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
+template <int kWaves>  // partition_size / 64
+__global__ __launch_bounds__(kWaves * kWave) void paged_attention_partition_kernel(
     float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
     const uint16_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
     int32_t num_kv_heads, int32_t block_size, int32_t max_blocks, int32_t max_parts,
     int64_t num_blocks, float scale, float k_scale, float v_scale) {
-  constexpr int P = kTiles * 16;
-  // per wave: probabilities of one 32-token chunk, [16 heads][32 tokens], hi and lo
-  __shared__ __align__(16) uint16_t p_lds[kPaWaves][2][16][kPaChunk + 8];
+  constexpr int P = kWaves * kPaWaveTokens;
+  constexpr int kPRow = kPaWaveTokens + 8;                // u16 per probability row
+  constexpr int kPBytes = kWaves * 2 * 16 * kPRow * 2;    // hi and lo, per wave
+  constexpr int kORow = kPaD + 4;                         // floats per output row
+  constexpr int kOBytes = kWaves * 16 * kORow * 4;        // partial outputs, per wave
+  // The probability slices are dead once the P.V products are done; the
+  // partial outputs reuse the same bytes after the first barrier.
+  __shared__ __align__(16) unsigned char lds[kPBytes > kOBytes ? kPBytes : kOBytes];
+  __shared__ float m_lds[kWaves][16], l_lds[kWaves][16];
+  uint16_t(*p_lds)[2][16][kPRow] = reinterpret_cast<uint16_t(*)[2][16][kPRow]>(lds);
+  float(*o_lds)[16][kORow] = reinterpret_cast<float(*)[16][kORow]>(lds);
 
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   const int col = lane & 15;  // operand row / result column
   const int grp = lane >> 4;  // K quarter / result row quarter
-  const int64_t unit = (int64_t)blockIdx.x * kPaWaves + wave;
-  if (unit >= (int64_t)num_seqs * num_kv_heads * max_parts) return;
-  const int32_t part = (int32_t)(unit % max_parts);
-  const int32_t kvh = (int32_t)((unit / max_parts) % num_kv_heads);
-  const int32_t s = (int32_t)(unit / ((int64_t)max_parts * num_kv_heads));
-  const int64_t L = context_lens[s];
-  const int64_t t_begin = (int64_t)part * P;
-  if (t_begin >= L) return;  // this partition holds no token
-  const int64_t t_end = (t_begin + P < L) ? t_begin + P : L;
+  // 32-bit index arithmetic: the host bounds the grid and every token index
+  // below 2^31.
+  const uint32_t unit = blockIdx.x;
+  const uint32_t part = unit % (uint32_t)max_parts;
+  const uint32_t kvh = (unit / (uint32_t)max_parts) % (uint32_t)num_kv_heads;
+  const uint32_t s = unit / ((uint32_t)max_parts * (uint32_t)num_kv_heads);
+  if (s >= (uint32_t)num_seqs) return;
+  const int32_t L = context_lens[s];
+  const int32_t t_begin = (int32_t)part * P;
+  if (t_begin >= L) return;  // uniform over the workgroup: no barrier is skipped by some waves only
+  const int32_t t_end = (L - t_begin > P) ? t_begin + P : L;
   const int32_t G = num_heads / num_kv_heads;
+  const int32_t tw = t_begin + wave * kPaWaveTokens;  // this wave's first token
 
-  // ---- query operands: row = head kvh*G + col (zero past G), K = d
+  // ---- query operands.  The contraction over d runs in the order that one
+  // 16-byte key row feeds: chunk c takes d = 16 (grp + 4 (c/2)) + 8 (c%2) + e.
+  // Rows past the group read the group's last head and are zeroed after.
+  const uint16_t* qrow =
+      query + ((int64_t)s * num_heads + (int64_t)kvh * G + (col < G ? col : G - 1)) * kPaD;
+  u32x4 qv[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qv[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * (grp + 4 * (c >> 1)) + 8 * (c & 1));
+
+  // ---- page of each of the wave's tiles (-1: no valid token in it).  The
+  // table entries are read without branches (column clamped into the row)
+  // so that the four reads are in flight together.
+  int32_t page[kPaTiles];  // table entries are int32: valid ids fit
+  int32_t tbl[kPaTiles];
+  const int32_t* trow = block_tables + (int64_t)s * max_blocks;
+  const int32_t jmax = max_blocks > 0 ? max_blocks - 1 : 0;
+#pragma unroll
+  for (int tt = 0; tt < kPaTiles; ++tt) {
+    const int32_t j = (int32_t)((uint32_t)(tw + tt * 16) / (uint32_t)block_size);
+    tbl[tt] = max_blocks > 0 ? trow[j < jmax ? j : jmax] : -1;
+  }
+#pragma unroll
+  for (int tt = 0; tt < kPaTiles; ++tt) {
+    const int32_t t0 = tw + tt * 16;
+    const int32_t j = (int32_t)((uint32_t)t0 / (uint32_t)block_size);
+    const int32_t pg = tbl[tt];
+    page[tt] = (t0 < t_end && j < max_blocks && pg >= 0 && pg < num_blocks) ? pg : -1;
+  }
+
+  // ---- every K and V load of the wave, issued before any of them is used.
+  // Tiles without a valid page read page 0 (in bounds) and are masked below.
+  const int64_t kv_head_keys = (int64_t)(kPaD / 16) * block_size * 16;  // bytes per (page, kv head)
+  const int64_t kv_head_vals = (int64_t)kPaD * block_size;
+  u32x4 kw[kPaTiles][2];  // tile tt: lane (col, grp) holds rows grp and grp + 4 of token col
+#pragma unroll
+  for (int tt = 0; tt < kPaTiles; ++tt) {
+    const int64_t pg = page[tt] >= 0 ? page[tt] : 0;
+    const int32_t off0 = (int32_t)((uint32_t)(tw + tt * 16) % (uint32_t)block_size);
+    const uint8_t* kp = key_cache + (pg * num_kv_heads + kvh) * kv_head_keys;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      kw[tt][h] = *reinterpret_cast<const u32x4*>(
+          kp + ((int64_t)(grp + 4 * h) * block_size + off0 + col) * 16);
+  }
+  // values: lane (col, grp) holds the 16 tokens of tile grp for d = 16n + col
+  int32_t page_v = page[0];
+  page_v = grp == 1 ? page[1] : page_v;
+  page_v = grp == 2 ? page[2] : page_v;
+  page_v = grp == 3 ? page[3] : page_v;
+  const int32_t tv = tw + grp * 16;
+  const uint8_t* vp = value_cache + ((int64_t)(page_v >= 0 ? page_v : 0) * num_kv_heads + kvh) * kv_head_vals +
+                      (uint32_t)tv % (uint32_t)block_size;
+  u32x4 vw[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    vw[n] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * n + col) * block_size);
+  // keep the scheduler from holding any of these loads back behind a use of
+  // an earlier one: the wave's whole share is requested before it waits
+  __builtin_amdgcn_sched_barrier(0);
+
   v8bf aq[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (col < G)
-      v = *reinterpret_cast<const u32x4*>(
-          query + ((int64_t)s * num_heads + kvh * G + col) * kPaD + c * 32 + grp * 8);
-    aq[c] = __builtin_bit_cast(v8bf, v);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    aq[c] = __builtin_bit_cast(v8bf, col < G ? qv[c] : zero);
   }
 
-  // ---- logits of every tile: lane holds token col, heads 4*grp + r
+  // ---- logits: lane holds token col of each tile for heads 4*grp + r
   const float qk_scale = scale * k_scale;
   const float neg_inf = -__builtin_inff();
-  const int64_t kv_head_keys = (int64_t)(kPaD / 16) * block_size * 16;  // bytes per (page, kv head)
-  float lg[kTiles][4];
-  int64_t tile_page[kTiles];
+  float lg[kPaTiles][4];
 #pragma unroll
-  for (int tt = 0; tt < kTiles; ++tt) {
-    const int64_t t0 = t_begin + tt * 16;
-    int64_t page = -1;
-    if (t0 < t_end) {
-      const int64_t j = t0 / block_size;
-      if (j < max_blocks) page = block_tables[(int64_t)s * max_blocks + j];
-      if (page >= num_blocks) page = -1;
-    }
-    tile_page[tt] = page;
-    const int64_t off0 = t0 % block_size;
+  for (int tt = 0; tt < kPaTiles; ++tt) {
     v4f acc = {0.f, 0.f, 0.f, 0.f};
-    if (page >= 0) {  // uniform over the wave
-      const uint8_t* kp = key_cache + (page * num_kv_heads + kvh) * kv_head_keys;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // d = 32c + 8*grp + e -> row d/16 = 2c + grp/2, column d%16 = 8*(grp%2) + e
-        const u32x2 w = *reinterpret_cast<const u32x2*>(
-            kp + ((int64_t)(2 * c + (grp >> 1)) * block_size + off0 + col) * 16 + 8 * (grp & 1));
-        acc = mfma_bf16(aq[c], fp8x8_to_bf16(w), acc);
-      }
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w = kw[tt][c >> 1];
+      const u32x2 half = (c & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
+      acc = mfma_bf16(aq[c], fp8x8_to_bf16(half), acc);
     }
-    const bool valid = page >= 0 && t0 + col < t_end;
+    const bool valid = page[tt] >= 0 && tw + tt * 16 + col < t_end;
     lg[tt][0] = valid ? acc.x * qk_scale : neg_inf;
     lg[tt][1] = valid ? acc.y * qk_scale : neg_inf;
     lg[tt][2] = valid ? acc.z * qk_scale : neg_inf;
     lg[tt][3] = valid ? acc.w * qk_scale : neg_inf;
   }
 
-  // ---- per-head max and exp-sum over the partition
+  // ---- per-head maximum and exp-sum over the wave's tokens
   float m[4], sum[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     float v = neg_inf;
 #pragma unroll
-    for (int tt = 0; tt < kTiles; ++tt) v = fmaxf(v, lg[tt][r]);
+    for (int tt = 0; tt < kPaTiles; ++tt) v = fmaxf(v, lg[tt][r]);
     m[r] = row16_max(v);
     float e = 0.0f;
 #pragma unroll
-    for (int tt = 0; tt < kTiles; ++tt) {
+    for (int tt = 0; tt < kPaTiles; ++tt) {
       const float p = (m[r] == neg_inf) ? 0.0f : __expf(lg[tt][r] - m[r]);
       lg[tt][r] = p;
       e += p;
@@ -177,102 +237,160 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
     sum[r] = row16_sum(e);
   }
 
-  // ---- partial output: 32 tokens per step, probabilities as bf16 hi + lo
+  // ---- probabilities to operand order through the wave's LDS slice, as a
+  // bf16 high part and the bf16 of the (exact) remainder
+#pragma unroll
+  for (int tt = 0; tt < kPaTiles; ++tt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = lg[tt][r];
+      const uint16_t hi = bf16_rn(p);
+      p_lds[wave][0][4 * grp + r][16 * tt + col] = hi;
+      p_lds[wave][1][4 * grp + r][16 * tt + col] = bf16_rn(p - __uint_as_float((uint32_t)hi << 16));
+    }
+  }
+  wave_sync();
+  // MFMA h of a d block takes K index 8*grp + e as token 16*grp + 8*h + e:
+  // probabilities from LDS, values from byte 8*h + e of the lane's 16.
+  v8bf ap[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      ap[h][x] = __builtin_bit_cast(
+          v8bf, *reinterpret_cast<const u32x4*>(&p_lds[wave][x][col][16 * grp + 8 * h]));
+
+  // value bytes of tokens without a valid page or past the context: zero
+  const int32_t live = page_v >= 0 ? t_end - tv : 0;
+  u32x4 keep;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int32_t n_live = live - 4 * q;
+    keep[q] = n_live >= 4 ? 0xFFFFFFFFu : n_live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - n_live)));
+  }
   v4f o[8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
-  const int64_t kv_head_vals = (int64_t)kPaD * block_size;  // bytes per (page, kv head)
-#pragma unroll
-  for (int k = 0; k < kTiles / 2; ++k) {
-    // transpose the chunk's probabilities to operand order through LDS
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int tt = 2 * k + half;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = lg[tt][r];
-        const uint16_t hi = bf16_rn(p);
-        const float rem = p - __uint_as_float((uint32_t)hi << 16);  // exact
-        p_lds[wave][0][4 * grp + r][16 * half + col] = hi;
-        p_lds[wave][1][4 * grp + r][16 * half + col] = bf16_rn(rem);
-      }
-    }
-    wave_sync();
-    const v8bf ap_hi = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&p_lds[wave][0][col][8 * grp]));
-    const v8bf ap_lo = __builtin_bit_cast(v8bf, *reinterpret_cast<const u32x4*>(&p_lds[wave][1][col][8 * grp]));
-    // values: tokens 8*grp .. +8 of the chunk lie in tile 2k + grp/2, offsets 8*(grp%2) ..
-    const int tt = 2 * k + (grp >> 1);
-    const int64_t page = tile_page[tt];
-    const int64_t t0 = t_begin + tt * 16 + 8 * (grp & 1);  // first token of this lane's 8
-    const int64_t off = t0 % block_size;
-    // tokens past the context may hold any bytes: zero their value codes
-    const int64_t n_live = t_end - t0;
-    uint32_t keep_lo = 0u, keep_hi = 0u;  // byte masks
-    if (page >= 0 && n_live > 0) {
-      keep_lo = n_live >= 4 ? 0xFFFFFFFFu : (0xFFFFFFFFu >> (8 * (4 - n_live)));
-      keep_hi = n_live >= 8 ? 0xFFFFFFFFu : (n_live <= 4 ? 0u : (0xFFFFFFFFu >> (8 * (8 - n_live))));
-    }
-    const uint8_t* vp = value_cache + (page >= 0 ? (page * num_kv_heads + kvh) * kv_head_vals : 0);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      u32x2 w = {0u, 0u};
-      if (keep_lo) w = *reinterpret_cast<const u32x2*>(vp + (int64_t)(16 * n + col) * block_size + off);
-      w.x &= keep_lo;
-      w.y &= keep_hi;
-      const v8bf bv = fp8x8_to_bf16(w);
-      o[n] = mfma_bf16(ap_hi, bv, o[n]);
-      o[n] = mfma_bf16(ap_lo, bv, o[n]);
-    }
-    wave_sync();  // the next chunk rewrites this wave's LDS slice
+  for (int n = 0; n < 8; ++n) {
+    const u32x4 w = vw[n] & keep;
+    const v8bf b0 = fp8x8_to_bf16(u32x2{w.x, w.y});
+    const v8bf b1 = fp8x8_to_bf16(u32x2{w.z, w.w});
+    v4f acc = {0.f, 0.f, 0.f, 0.f};
+    acc = mfma_bf16(ap[0][0], b0, acc);
+    acc = mfma_bf16(ap[0][1], b0, acc);
+    acc = mfma_bf16(ap[1][0], b1, acc);
+    acc = mfma_bf16(ap[1][1], b1, acc);
+    o[n] = acc;
   }
 
-  // ---- normalised partial output, exp-sum and max of each real head
+  // ---- combine the waves: common maximum, rescaled exp-sums and outputs
+  if (col == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m_lds[wave][4 * grp + r] = m[r];
+      l_lds[wave][4 * grp + r] = sum[r];
+    }
+  }
+  __syncthreads();  // also ends every read of the probability slices
+  float M[4], Lsum[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float mx = neg_inf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, m_lds[w][4 * grp + r]);
+    float l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = m_lds[w][4 * grp + r];
+      if (mw != neg_inf) l += l_lds[w][4 * grp + r] * __expf(mw - mx);
+    }
+    M[r] = mx;
+    Lsum[r] = l;
+    const float f = (m[r] == neg_inf) ? 0.0f : __expf(m[r] - mx);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) o_lds[wave][4 * grp + r][16 * n + col] = o[n][r] * f;
+  }
+  __syncthreads();
+  constexpr int kNPerWave = 8 / kWaves;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * grp + r;
     if (row >= G) continue;
-    const int64_t h = (int64_t)kvh * G + row;
-    const int64_t sh = (int64_t)s * num_heads + h;
-    const float inv = sum[r] > 0.0f ? v_scale / sum[r] : 0.0f;
+    const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + row;
+    const float inv = Lsum[r] > 0.0f ? v_scale / Lsum[r] : 0.0f;
     float* dst = tmp_out + (sh * max_parts + part) * kPaD;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) dst[16 * n + col] = o[n][r] * inv;
-    if (col == 0) {
-      exp_sums[sh * max_parts + part] = sum[r];
-      max_logits[sh * max_parts + part] = m[r];
+    for (int i = 0; i < kNPerWave; ++i) {
+      const int n = wave * kNPerWave + i;
+      float x = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) x += o_lds[w][row][16 * n + col];
+      dst[16 * n + col] = x * inv;
+    }
+    if (wave == 0 && col == 0) {
+      exp_sums[sh * max_parts + part] = Lsum[r];
+      max_logits[sh * max_parts + part] = M[r];
     }
   }
 }
 
+// One wave per (sequence, head): lanes take the partitions' exp-sums and
+// maxima in parallel, then the weighted partial outputs (two d per lane).
 __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ exp_sums,
     const float* __restrict__ max_logits, const float* __restrict__ tmp_out,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
     int32_t max_parts, int32_t partition_size) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t sh = (int64_t)blockIdx.x * kPaWaves + threadIdx.x / kWave;
-  if (sh >= (int64_t)num_seqs * num_heads) return;
-  const int32_t s = (int32_t)(sh / num_heads);
-  const int64_t L = context_lens[s];
-  int64_t nparts = L > 0 ? (L + partition_size - 1) / partition_size : 0;
+  const uint32_t sh = blockIdx.x * kPaWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (sh >= (uint32_t)num_seqs * (uint32_t)num_heads) return;
+  const uint32_t s = sh / (uint32_t)num_heads;
+  const int32_t L = context_lens[s];
+  int32_t nparts = L > 0 ? (L - 1) / partition_size + 1 : 0;
   if (nparts > max_parts) nparts = max_parts;
-  const float* es = exp_sums + sh * max_parts;
-  const float* ml = max_logits + sh * max_parts;
-  float M = -__builtin_inff();
-  for (int64_t p = 0; p < nparts; ++p)
-    if (es[p] > 0.0f) M = fmaxf(M, ml[p]);
-  float a0 = 0.0f, a1 = 0.0f, W = 0.0f;
-  for (int64_t p = 0; p < nparts; ++p) {
-    if (!(es[p] > 0.0f)) continue;
-    const float w = es[p] * __expf(ml[p] - M);
-    const float* o = tmp_out + (sh * max_parts + p) * kPaD;
-    a0 = __builtin_fmaf(w, o[lane], a0);
-    a1 = __builtin_fmaf(w, o[lane + 64], a1);
-    W += w;
+  const float* es = exp_sums + (int64_t)sh * max_parts;
+  const float* ml = max_logits + (int64_t)sh * max_parts;
+  const float neg_inf = -__builtin_inff();
+  float M = neg_inf;
+  for (int32_t b = 0; b < nparts; b += kWave) {
+    const int32_t p = b + lane;
+    if (p < nparts && es[p] > 0.0f) M = fmaxf(M, ml[p]);
   }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
+  float W = 0.0f, a0 = 0.0f, a1 = 0.0f;
+  const float* o = tmp_out + (int64_t)sh * max_parts * kPaD + 2 * lane;
+  for (int32_t b = 0; b < nparts; b += kWave) {
+    const int32_t p = b + lane;
+    float wl = 0.0f;
+    if (p < nparts && es[p] > 0.0f) wl = es[p] * __expf(ml[p] - M);
+    W += wl;
+    const int cnt = nparts - b < kWave ? nparts - b : kWave;
+    // every partition row below nparts was written by this call, with
+    // finite values, so rows of weight 0 add exactly 0
+    int i = 0;
+    for (; i + 8 <= cnt; i += 8) {  // eight rows in flight
+      f32x2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x2*>(o + (int64_t)(b + i + u) * kPaD);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = __shfl(wl, i + u);
+        a0 = __builtin_fmaf(w, v[u].x, a0);
+        a1 = __builtin_fmaf(w, v[u].y, a1);
+      }
+    }
+    for (; i < cnt; ++i) {
+      const float w = __shfl(wl, i);
+      const f32x2 v = *reinterpret_cast<const f32x2*>(o + (int64_t)(b + i) * kPaD);
+      a0 = __builtin_fmaf(w, v.x, a0);
+      a1 = __builtin_fmaf(w, v.y, a1);
+    }
+  }
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) W += __shfl_xor(W, d);
   const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-  out[sh * kPaD + lane] = bf16_rn(a0 * inv);
-  out[sh * kPaD + lane + 64] = bf16_rn(a1 * inv);
+  const uint32_t packed = (uint32_t)bf16_rn(a0 * inv) | ((uint32_t)bf16_rn(a1 * inv) << 16);
+  *reinterpret_cast<uint32_t*>(out + (int64_t)sh * kPaD + 2 * lane) = packed;
 }
 
 }  // namespace
@@ -281,20 +399,38 @@ int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t strea
   const int32_t P = a.partition_size;
   const int32_t max_parts = (a.max_context_len + P - 1) / P;
   const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * max_parts;
-  const int64_t blocks = (units + kPaWaves - 1) / kPaWaves;
-  auto kernel = paged_attention_partition_kernel<16>;
-  switch (P / 16) {
-    case 2: kernel = paged_attention_partition_kernel<2>; break;
-    case 4: kernel = paged_attention_partition_kernel<4>; break;
-    case 8: kernel = paged_attention_partition_kernel<8>; break;
-    default: break;
-  }
-  if (blocks > 0) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kPaThreads), 0, stream, a.exp_sums,
-                       a.max_logits, a.tmp_out, a.query, a.key_cache, a.value_cache,
-                       a.block_tables, a.context_lens, a.num_seqs, a.num_heads, a.num_kv_heads,
-                       a.block_size, a.max_blocks_per_seq, max_parts, a.num_blocks, a.scale,
-                       a.k_scale, a.v_scale);
+  if (units > 0) {
+    const dim3 grid((unsigned)units);
+    switch (P) {
+      case 64:
+        hipLaunchKernelGGL(paged_attention_partition_kernel<1>, grid, dim3(kWave), 0, stream,
+                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
+                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
+                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
+        break;
+      case 128:
+        hipLaunchKernelGGL(paged_attention_partition_kernel<2>, grid, dim3(2 * kWave), 0, stream,
+                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
+                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
+                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
+        break;
+      case 256:
+        hipLaunchKernelGGL(paged_attention_partition_kernel<4>, grid, dim3(4 * kWave), 0, stream,
+                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
+                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
+                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
+        break;
+      default:
+        hipLaunchKernelGGL(paged_attention_partition_kernel<8>, grid, dim3(8 * kWave), 0, stream,
+                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
+                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
+                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
+        break;
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }

@@ -67,10 +67,11 @@ def check(got, ref, b):
 @pytest.mark.parametrize("H,KVH,B,P", [
     (8, 1, 16, 256),     # 8 query heads per KV head
     (32, 2, 16, 64),     # 16 per KV head (the largest group)
-    (4, 4, 32, 32),      # no grouping, 32-token pages, smallest partition
+    (4, 4, 32, 64),      # no grouping, 32-token pages, smallest partition
     (14, 2, 16, 128),    # a group of 7
     (64, 8, 16, 256),    # Llama-3.1-70B heads
     (16, 1, 64, 256),    # 64-token pages
+    (24, 2, 16, 512),    # a group of 12, the largest partition
 ])
 def test_shapes(H, KVH, B, P):
     banner(f"paged attention H={H} KVH={KVH} B={B} P={P}")
@@ -82,12 +83,12 @@ def test_shapes(H, KVH, B, P):
 
 
 def test_long_contexts_many_partitions():
-    banner("paged attention long contexts, P=32")
+    banner("paged attention long contexts, P=64 and 512")
     lens = [4100, 3000, 2049]
     c = workloads.paged_attention_case(9, len(lens), 16, 2, lens=lens)
     ref, b = reference(c)
-    check(run(c, 32), ref, b)
-    check(run(c, 256), ref, b)
+    check(run(c, 64), ref, b)
+    check(run(c, 512), ref, b)
 
 
 def test_edges_empty_invalid_pages_and_stale_bytes():
