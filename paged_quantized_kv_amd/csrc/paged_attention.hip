@@ -35,6 +35,8 @@
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
 // and rounds to bf16.  A sequence without a valid token gets a zero row;
 // tokens whose page id is outside [0, num_blocks) are left out.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "pkv.h"
@@ -53,87 +55,131 @@ constexpr int kPaWaves = kPaThreads / kWave;
 constexpr int kPaD = 128;        // head_size
 constexpr int kPaWaveTokens = 64;  // tokens per wave in the partition kernel
 constexpr int kPaTiles = kPaWaveTokens / 16;
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kLazy = 8.0f;  // log2 of the largest weight before a rescale
 
 __device__ __forceinline__ v4f mfma_bf16(const v8bf a, const v8bf b, const v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// 8 E4M3 codes (little-endian in two dwords) -> 8 bf16, exact.
+// 8 E4M3 codes (little-endian in two dwords) -> 8 bf16, exact: the gfx950
+// scaled converter with unit scale, two codes per instruction (every E4M3
+// value has at most 4 significant bits and lies in bf16's range).
 __device__ __forceinline__ v8bf fp8x8_to_bf16(u32x2 w) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.x, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)w.y, true);
-  // a binary32 value with at most 8 significant bits is its own top half
-  v8bf r;
-  r[0] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(a.x) >> 16));
-  r[1] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(a.y) >> 16));
-  r[2] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(b.x) >> 16));
-  r[3] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(b.y) >> 16));
-  r[4] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(c.x) >> 16));
-  r[5] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(c.y) >> 16));
-  r[6] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(d.x) >> 16));
-  r[7] = __builtin_bit_cast(__bf16, (uint16_t)(__float_as_uint(d.y) >> 16));
-  return r;
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Max / sum over the 16 lanes of each lane row (lanes 16g .. 16g+15).
+// Lane exchange inside rows of 16 lanes by DPP (no LDS round trip).
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
+}
+// Max / sum over the 16 lanes of each row: swap neighbours, swap pairs
+// (quad permutations), then the mirrored lane of the half row and of the
+// row, which pairs up the quads and then the halves.
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
 __device__ __forceinline__ float row16_max(float v) {
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) v = fmaxf(v, __shfl_xor(v, d));
-  return v;
+  v = fmaxf(v, dpp<kDppXor1>(v));
+  v = fmaxf(v, dpp<kDppXor2>(v));
+  v = fmaxf(v, dpp<kDppHalfMirror>(v));
+  return fmaxf(v, dpp<kDppMirror>(v));
 }
 __device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d);
-  return v;
+  v += dpp<kDppXor1>(v);
+  v += dpp<kDppXor2>(v);
+  v += dpp<kDppHalfMirror>(v);
+  return v + dpp<kDppMirror>(v);
 }
 
 __device__ __forceinline__ uint16_t bf16_rn(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-template <int kWaves>  // partition_size / 64
-__global__ __launch_bounds__(kWaves * kWave) void paged_attention_partition_kernel(
+// Pages of the four 16-token tiles of the 64-token block starting at token
+// tb: table entries read without branches (column clamped into the row), so
+// that the four scalar reads are in flight together.
+struct BlockTable {
+  int32_t e[kPaTiles];
+};
+
+__device__ __forceinline__ BlockTable read_block_table(const int32_t* trow, int32_t max_blocks,
+                                                       const FastDiv& bdiv, int32_t tb) {
+  BlockTable t;
+  const int32_t jmax = max_blocks > 0 ? max_blocks - 1 : 0;
+#pragma unroll
+  for (int tt = 0; tt < kPaTiles; ++tt) {
+    const int32_t j = (int32_t)bdiv.div((uint32_t)(tb + tt * 16));
+    t.e[tt] = max_blocks > 0 ? trow[j < jmax ? j : jmax] : -1;
+  }
+  return t;
+}
+
+// Valid page id of each tile, or -1 (tile past the context, column past the
+// row, id outside [0, num_blocks)).
+__device__ __forceinline__ void block_pages(const BlockTable& t, int32_t tb, int32_t t_end,
+                                            int32_t max_blocks, const FastDiv& bdiv,
+                                            int64_t num_blocks, int32_t (&page)[kPaTiles]) {
+#pragma unroll
+  for (int tt = 0; tt < kPaTiles; ++tt) {
+    const int32_t t0 = tb + tt * 16;
+    const int32_t j = (int32_t)bdiv.div((uint32_t)t0);
+    const int32_t pg = t.e[tt];
+    page[tt] = (t0 < t_end && j < max_blocks && pg >= 0 && pg < num_blocks) ? pg : -1;
+  }
+}
+
+// One wave per (sequence, kv head, partition); a workgroup holds the waves of
+// four consecutive kv heads of one (sequence, partition), so that all of
+// them have work or none has.  There is no barrier: waves only share the
+// workgroup's LDS through disjoint slices.
+__global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
     float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
     const uint16_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t block_size, int32_t max_blocks, int32_t max_parts,
-    int64_t num_blocks, float scale, float k_scale, float v_scale) {
-  constexpr int P = kWaves * kPaWaveTokens;
-  constexpr int kPRow = kPaWaveTokens + 8;                // u16 per probability row
-  constexpr int kPBytes = kWaves * 2 * 16 * kPRow * 2;    // hi and lo, per wave
-  constexpr int kORow = kPaD + 4;                         // floats per output row
-  constexpr int kOBytes = kWaves * 16 * kORow * 4;        // partial outputs, per wave
-  // The probability slices are dead once the P.V products are done; the
-  // partial outputs reuse the same bytes after the first barrier.
-  __shared__ __align__(16) unsigned char lds[kPBytes > kOBytes ? kPBytes : kOBytes];
-  __shared__ float m_lds[kWaves][16], l_lds[kWaves][16];
-  uint16_t(*p_lds)[2][16][kPRow] = reinterpret_cast<uint16_t(*)[2][16][kPRow]>(lds);
-  float(*o_lds)[16][kORow] = reinterpret_cast<float(*)[16][kORow]>(lds);
+    int32_t num_kv_heads, int32_t block_size, FastDiv bdiv, int32_t max_blocks, int32_t max_parts,
+    int32_t partition_size, int64_t num_blocks, float scale, float k_scale, float v_scale) {
+  constexpr int kPRow = kPaWaveTokens + 8;  // u16 per probability row
+  __shared__ __align__(16) uint16_t p_lds[kPaWaves][2][16][kPRow];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   const int col = lane & 15;  // operand row / result column
   const int grp = lane >> 4;  // K quarter / result row quarter
   // 32-bit index arithmetic: the host bounds the grid and every token index
-  // below 2^31.
+  // below 2^31.  Partition-major order: the workgroups of all sequences'
+  // first partitions come first.
+  const uint32_t groups = ((uint32_t)num_kv_heads + kPaWaves - 1) / kPaWaves;
   const uint32_t unit = blockIdx.x;
-  const uint32_t part = unit % (uint32_t)max_parts;
-  const uint32_t kvh = (unit / (uint32_t)max_parts) % (uint32_t)num_kv_heads;
-  const uint32_t s = unit / ((uint32_t)max_parts * (uint32_t)num_kv_heads);
-  if (s >= (uint32_t)num_seqs) return;
+  const uint32_t kvh = (unit % groups) * kPaWaves + wave;
+  const uint32_t sp = unit / groups;
+  const uint32_t s = sp % (uint32_t)num_seqs;
+  const uint32_t part = sp / (uint32_t)num_seqs;
+  if (kvh >= (uint32_t)num_kv_heads || part >= (uint32_t)max_parts) return;
   const int32_t L = context_lens[s];
-  const int32_t t_begin = (int32_t)part * P;
-  if (t_begin >= L) return;  // uniform over the workgroup: no barrier is skipped by some waves only
-  const int32_t t_end = (L - t_begin > P) ? t_begin + P : L;
+  const int32_t t_begin = (int32_t)part * partition_size;
+  if (t_begin >= L) return;
+  const int32_t t_end = (L - t_begin > partition_size) ? t_begin + partition_size : L;
+  const int32_t nblk = (t_end - t_begin + kPaWaveTokens - 1) / kPaWaveTokens;
   const int32_t G = num_heads / num_kv_heads;
-  const int32_t tw = t_begin + wave * kPaWaveTokens;  // this wave's first token
+  const int32_t* trow = block_tables + (int64_t)s * max_blocks;
+  const int64_t kv_head_keys = (int64_t)(kPaD / 16) * block_size * 16;  // bytes per (page, kv head)
+  const int64_t kv_head_vals = (int64_t)kPaD * block_size;
+  const uint8_t* kbase = key_cache + (int64_t)kvh * kv_head_keys;
+  const uint8_t* vbase = value_cache + (int64_t)kvh * kv_head_vals;
+  const int64_t kpage = (int64_t)num_kv_heads * kv_head_keys;  // bytes per page, all kv heads
+  const int64_t vpage = (int64_t)num_kv_heads * kv_head_vals;
 
-  // ---- query operands.  The contraction over d runs in the order that one
-  // 16-byte key row feeds: chunk c takes d = 16 (grp + 4 (c/2)) + 8 (c%2) + e.
-  // Rows past the group read the group's last head and are zeroed after.
+  // ---- query rows: chunk c of the contraction takes d = 16 (grp + 4 (c/2)) +
+  // 8 (c%2) + e, the order in which one 16-byte key row feeds it.  Rows past
+  // the group read the group's last head and are zeroed when used.
   const uint16_t* qrow =
       query + ((int64_t)s * num_heads + (int64_t)kvh * G + (col < G ? col : G - 1)) * kPaD;
   u32x4 qv[4];
@@ -141,56 +187,52 @@ __global__ __launch_bounds__(kWaves * kWave) void paged_attention_partition_kern
   for (int c = 0; c < 4; ++c)
     qv[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * (grp + 4 * (c >> 1)) + 8 * (c & 1));
 
-  // ---- page of each of the wave's tiles (-1: no valid token in it).  The
-  // table entries are read without branches (column clamped into the row)
-  // so that the four reads are in flight together.
-  int32_t page[kPaTiles];  // table entries are int32: valid ids fit
-  int32_t tbl[kPaTiles];
-  const int32_t* trow = block_tables + (int64_t)s * max_blocks;
-  const int32_t jmax = max_blocks > 0 ? max_blocks - 1 : 0;
-#pragma unroll
-  for (int tt = 0; tt < kPaTiles; ++tt) {
-    const int32_t j = (int32_t)((uint32_t)(tw + tt * 16) / (uint32_t)block_size);
-    tbl[tt] = max_blocks > 0 ? trow[j < jmax ? j : jmax] : -1;
-  }
-#pragma unroll
-  for (int tt = 0; tt < kPaTiles; ++tt) {
-    const int32_t t0 = tw + tt * 16;
-    const int32_t j = (int32_t)((uint32_t)t0 / (uint32_t)block_size);
-    const int32_t pg = tbl[tt];
-    page[tt] = (t0 < t_end && j < max_blocks && pg >= 0 && pg < num_blocks) ? pg : -1;
-  }
-
-  // ---- every K and V load of the wave, issued before any of them is used.
-  // Tiles without a valid page read page 0 (in bounds) and are masked below.
-  const int64_t kv_head_keys = (int64_t)(kPaD / 16) * block_size * 16;  // bytes per (page, kv head)
-  const int64_t kv_head_vals = (int64_t)kPaD * block_size;
-  u32x4 kw[kPaTiles][2];  // tile tt: lane (col, grp) holds rows grp and grp + 4 of token col
-#pragma unroll
-  for (int tt = 0; tt < kPaTiles; ++tt) {
-    const int64_t pg = page[tt] >= 0 ? page[tt] : 0;
-    const int32_t off0 = (int32_t)((uint32_t)(tw + tt * 16) % (uint32_t)block_size);
-    const uint8_t* kp = key_cache + (pg * num_kv_heads + kvh) * kv_head_keys;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      kw[tt][h] = *reinterpret_cast<const u32x4*>(
-          kp + ((int64_t)(grp + 4 * h) * block_size + off0 + col) * 16);
-  }
-  // values: lane (col, grp) holds the 16 tokens of tile grp for d = 16n + col
-  int32_t page_v = page[0];
-  page_v = grp == 1 ? page[1] : page_v;
-  page_v = grp == 2 ? page[2] : page_v;
-  page_v = grp == 3 ? page[3] : page_v;
-  const int32_t tv = tw + grp * 16;
-  const uint8_t* vp = value_cache + ((int64_t)(page_v >= 0 ? page_v : 0) * num_kv_heads + kvh) * kv_head_vals +
-                      (uint32_t)tv % (uint32_t)block_size;
+  // Loads of one 64-token block.  Keys: lane (col, grp) holds rows grp and
+  // grp + 4 of token col of each tile.  Values: the 16 tokens of tile grp for
+  // d = 16n + col.  Tiles without a valid page read page 0 (in bounds) and
+  // are masked when used.
+  u32x4 kw[kPaTiles][2];
   u32x4 vw[8];
+  auto issue_keys = [&](const int32_t (&pg)[kPaTiles], int32_t tb) {
 #pragma unroll
-  for (int n = 0; n < 8; ++n)
-    vw[n] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * n + col) * block_size);
-  // keep the scheduler from holding any of these loads back behind a use of
-  // an earlier one: the wave's whole share is requested before it waits
-  __builtin_amdgcn_sched_barrier(0);
+    for (int tt = 0; tt < kPaTiles; ++tt) {
+      const uint32_t t0 = (uint32_t)(tb + tt * 16);
+      const int32_t off0 = (int32_t)(t0 - bdiv.div(t0) * (uint32_t)block_size);
+      const uint8_t* kp = kbase + (int64_t)(pg[tt] >= 0 ? pg[tt] : 0) * kpage;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        kw[tt][h] = *reinterpret_cast<const u32x4*>(
+            kp + ((int64_t)(grp + 4 * h) * block_size + off0 + col) * 16);
+    }
+  };
+  // page of tile grp, by masks: a select chain on grp would be turned into an
+  // indexed (scratch) access to the array
+  const uint32_t sel0 = 0u - (uint32_t)(grp == 0), sel1 = 0u - (uint32_t)(grp == 1);
+  const uint32_t sel2 = 0u - (uint32_t)(grp == 2), sel3 = 0u - (uint32_t)(grp == 3);
+  auto lane_page = [&](const int32_t (&pg)[kPaTiles]) {
+    return (int32_t)(((uint32_t)pg[0] & sel0) | ((uint32_t)pg[1] & sel1) |
+                     ((uint32_t)pg[2] & sel2) | ((uint32_t)pg[3] & sel3));
+  };
+  auto issue_values = [&](const int32_t (&pg)[kPaTiles], int32_t tb) {
+    const int32_t pv = lane_page(pg);
+    const uint32_t t0 = (uint32_t)(tb + grp * 16);
+    const uint8_t* vp = vbase + (int64_t)(pv >= 0 ? pv : 0) * vpage +
+                        (t0 - bdiv.div(t0) * (uint32_t)block_size);
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+      vw[n] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * n + col) * block_size);
+  };
+
+  // ---- prologue: block 0's pages and loads; block 1's table entries
+  int32_t page[kPaTiles];
+  {
+    const BlockTable t0 = read_block_table(trow, max_blocks, bdiv, t_begin);
+    block_pages(t0, t_begin, t_end, max_blocks, bdiv, num_blocks, page);
+  }
+  issue_keys(page, t_begin);
+  issue_values(page, t_begin);
+  BlockTable next_tbl = read_block_table(trow, max_blocks, bdiv, t_begin + kPaWaveTokens);
+  __builtin_amdgcn_sched_barrier(0);  // block 0 is requested before anything waits
 
   v8bf aq[4];
 #pragma unroll
@@ -199,136 +241,155 @@ __global__ __launch_bounds__(kWaves * kWave) void paged_attention_partition_kern
     aq[c] = __builtin_bit_cast(v8bf, col < G ? qv[c] : zero);
   }
 
-  // ---- logits: lane holds token col of each tile for heads 4*grp + r
-  const float qk_scale = scale * k_scale;
+  // logits in units of log2(e), so that each weight is one hardware exp2
+  const float qk_scale = (scale * k_scale) * kLog2e;
   const float neg_inf = -__builtin_inff();
-  float lg[kPaTiles][4];
-#pragma unroll
-  for (int tt = 0; tt < kPaTiles; ++tt) {
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 w = kw[tt][c >> 1];
-      const u32x2 half = (c & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
-      acc = mfma_bf16(aq[c], fp8x8_to_bf16(half), acc);
-    }
-    const bool valid = page[tt] >= 0 && tw + tt * 16 + col < t_end;
-    lg[tt][0] = valid ? acc.x * qk_scale : neg_inf;
-    lg[tt][1] = valid ? acc.y * qk_scale : neg_inf;
-    lg[tt][2] = valid ? acc.z * qk_scale : neg_inf;
-    lg[tt][3] = valid ? acc.w * qk_scale : neg_inf;
-  }
-
-  // ---- per-head maximum and exp-sum over the wave's tokens
-  float m[4], sum[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float v = neg_inf;
-#pragma unroll
-    for (int tt = 0; tt < kPaTiles; ++tt) v = fmaxf(v, lg[tt][r]);
-    m[r] = row16_max(v);
-    float e = 0.0f;
-#pragma unroll
-    for (int tt = 0; tt < kPaTiles; ++tt) {
-      const float p = (m[r] == neg_inf) ? 0.0f : __expf(lg[tt][r] - m[r]);
-      lg[tt][r] = p;
-      e += p;
-    }
-    sum[r] = row16_sum(e);
-  }
-
-  // ---- probabilities to operand order through the wave's LDS slice, as a
-  // bf16 high part and the bf16 of the (exact) remainder
-#pragma unroll
-  for (int tt = 0; tt < kPaTiles; ++tt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = lg[tt][r];
-      const uint16_t hi = bf16_rn(p);
-      p_lds[wave][0][4 * grp + r][16 * tt + col] = hi;
-      p_lds[wave][1][4 * grp + r][16 * tt + col] = bf16_rn(p - __uint_as_float((uint32_t)hi << 16));
-    }
-  }
-  wave_sync();
-  // MFMA h of a d block takes K index 8*grp + e as token 16*grp + 8*h + e:
-  // probabilities from LDS, values from byte 8*h + e of the lane's 16.
-  v8bf ap[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-      ap[h][x] = __builtin_bit_cast(
-          v8bf, *reinterpret_cast<const u32x4*>(&p_lds[wave][x][col][16 * grp + 8 * h]));
-
-  // value bytes of tokens without a valid page or past the context: zero
-  const int32_t live = page_v >= 0 ? t_end - tv : 0;
-  u32x4 keep;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int32_t n_live = live - 4 * q;
-    keep[q] = n_live >= 4 ? 0xFFFFFFFFu : n_live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - n_live)));
-  }
+  float m_run[4] = {neg_inf, neg_inf, neg_inf, neg_inf};
+  float l_run[4] = {0.f, 0.f, 0.f, 0.f};
   v4f o[8];
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const u32x4 w = vw[n] & keep;
-    const v8bf b0 = fp8x8_to_bf16(u32x2{w.x, w.y});
-    const v8bf b1 = fp8x8_to_bf16(u32x2{w.z, w.w});
-    v4f acc = {0.f, 0.f, 0.f, 0.f};
-    acc = mfma_bf16(ap[0][0], b0, acc);
-    acc = mfma_bf16(ap[0][1], b0, acc);
-    acc = mfma_bf16(ap[1][0], b1, acc);
-    acc = mfma_bf16(ap[1][1], b1, acc);
-    o[n] = acc;
-  }
+  for (int n = 0; n < 8; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // ---- combine the waves: common maximum, rescaled exp-sums and outputs
-  if (col == 0) {
+  // One block: logits, running softmax, P.V.  With kPrefetch the next
+  // block's keys are requested as soon as the key registers are free and its
+  // values as soon as the value registers are; the last block is peeled off
+  // so that every iteration of the loop issues the same loads (the waits
+  // then keep exactly the newest block in flight).
+  auto block = [&](int32_t b, auto prefetch) {
+    constexpr bool kPrefetch = decltype(prefetch)::value;
+    const int32_t tb = t_begin + b * kPaWaveTokens;
+    BlockTable tbl2;
+    if constexpr (kPrefetch)  // table entries two blocks ahead
+      tbl2 = read_block_table(trow, max_blocks, bdiv, tb + 2 * kPaWaveTokens);
+
+    // ---- logits of the block: lane holds token col of each tile, heads 4*grp + r
+    float lg[kPaTiles][4];
+#pragma unroll
+    for (int tt = 0; tt < kPaTiles; ++tt) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u32x4 w = kw[tt][c >> 1];
+        const u32x2 half = (c & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
+        acc = mfma_bf16(aq[c], fp8x8_to_bf16(half), acc);
+      }
+      const bool valid = page[tt] >= 0 && tb + tt * 16 + col < t_end;
+      lg[tt][0] = valid ? acc.x * qk_scale : neg_inf;
+      lg[tt][1] = valid ? acc.y * qk_scale : neg_inf;
+      lg[tt][2] = valid ? acc.z * qk_scale : neg_inf;
+      lg[tt][3] = valid ? acc.w * qk_scale : neg_inf;
+    }
+    int32_t next_page[kPaTiles];
+    if constexpr (kPrefetch) {
+      block_pages(next_tbl, tb + kPaWaveTokens, t_end, max_blocks, bdiv, num_blocks, next_page);
+      issue_keys(next_page, tb + kPaWaveTokens);
+    }
+
+    // ---- softmax reference point per head.  It only moves when the block's
+    // maximum exceeds it by more than 2^kLazy (weights stay <= 2^kLazy), so
+    // the output and exp-sum so far are rarely rescaled; the result is the
+    // same sum with other intermediate scalings.
+    float m_blk[4];
+    bool move = false;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m_lds[wave][4 * grp + r] = m[r];
-      l_lds[wave][4 * grp + r] = sum[r];
+      float v = neg_inf;
+#pragma unroll
+      for (int tt = 0; tt < kPaTiles; ++tt) v = fmaxf(v, lg[tt][r]);
+      m_blk[r] = row16_max(v);
+      move |= m_blk[r] > m_run[r] + kLazy;
     }
-  }
-  __syncthreads();  // also ends every read of the probability slices
-  float M[4], Lsum[4];
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {  // uniform over the wave
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float mx = neg_inf;
+      for (int r = 0; r < 4; ++r) {
+        const float m_new = m_blk[r] > m_run[r] + kLazy ? m_blk[r] : m_run[r];
+        const float alpha =
+            (m_run[r] == neg_inf) ? 0.0f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
+        l_run[r] *= alpha;
+        m_run[r] = m_new;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, m_lds[w][4 * grp + r]);
-    float l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float mw = m_lds[w][4 * grp + r];
-      if (mw != neg_inf) l += l_lds[w][4 * grp + r] * __expf(mw - mx);
+        for (int n = 0; n < 8; ++n) o[n][r] *= alpha;
+      }
     }
-    M[r] = mx;
-    Lsum[r] = l;
-    const float f = (m[r] == neg_inf) ? 0.0f : __expf(m[r] - mx);
 #pragma unroll
-    for (int n = 0; n < 8; ++n) o_lds[wave][4 * grp + r][16 * n + col] = o[n][r] * f;
-  }
-  __syncthreads();
-  constexpr int kNPerWave = 8 / kWaves;
+    for (int r = 0; r < 4; ++r) {
+      float e = 0.0f;
+#pragma unroll
+      for (int tt = 0; tt < kPaTiles; ++tt) {
+        const float p = (m_run[r] == neg_inf) ? 0.0f : __builtin_amdgcn_exp2f(lg[tt][r] - m_run[r]);
+        lg[tt][r] = p;
+        e += p;
+      }
+      l_run[r] += row16_sum(e);
+    }
+
+    // ---- probabilities to operand order through the wave's LDS slice, as a
+    // bf16 high part and the bf16 of the (exact) remainder
+#pragma unroll
+    for (int tt = 0; tt < kPaTiles; ++tt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = lg[tt][r];
+        const uint16_t hi = bf16_rn(p);
+        p_lds[wave][0][4 * grp + r][16 * tt + col] = hi;
+        p_lds[wave][1][4 * grp + r][16 * tt + col] =
+            bf16_rn(p - __uint_as_float((uint32_t)hi << 16));
+      }
+    }
+    wave_sync();
+    // MFMA h of a d block takes K index 8*grp + e as token 16*grp + 8*h + e:
+    // probabilities from LDS, values from byte 8*h + e of the lane's 16.
+    v8bf ap[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+        ap[h][x] = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const u32x4*>(&p_lds[wave][x][col][16 * grp + 8 * h]));
+    wave_sync();  // the next block rewrites the slice
+
+    // value bytes of tokens without a valid page or past the context: zero
+    const int32_t live = lane_page(page) >= 0 ? t_end - (tb + grp * 16) : 0;
+    u32x4 keep;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int32_t n_live = live - 4 * q;
+      keep[q] = n_live >= 4 ? 0xFFFFFFFFu : n_live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - n_live)));
+    }
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const u32x4 w = vw[n] & keep;
+      const v8bf b0 = fp8x8_to_bf16(u32x2{w.x, w.y});
+      const v8bf b1 = fp8x8_to_bf16(u32x2{w.z, w.w});
+      o[n] = mfma_bf16(ap[0][0], b0, o[n]);
+      o[n] = mfma_bf16(ap[0][1], b0, o[n]);
+      o[n] = mfma_bf16(ap[1][0], b1, o[n]);
+      o[n] = mfma_bf16(ap[1][1], b1, o[n]);
+    }
+    if constexpr (kPrefetch) {
+      __builtin_amdgcn_sched_barrier(0);  // the values are used before they are replaced
+      issue_values(next_page, tb + kPaWaveTokens);
+#pragma unroll
+      for (int tt = 0; tt < kPaTiles; ++tt) page[tt] = next_page[tt];
+      next_tbl = tbl2;
+    }
+  };
+  for (int32_t b = 0; b + 1 < nblk; ++b) block(b, std::true_type{});
+  block(nblk - 1, std::false_type{});
+
+  // ---- normalised partial output, exp-sum and maximum of each real head
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * grp + r;
     if (row >= G) continue;
     const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + row;
-    const float inv = Lsum[r] > 0.0f ? v_scale / Lsum[r] : 0.0f;
+    const float inv = l_run[r] > 0.0f ? v_scale / l_run[r] : 0.0f;
     float* dst = tmp_out + (sh * max_parts + part) * kPaD;
 #pragma unroll
-    for (int i = 0; i < kNPerWave; ++i) {
-      const int n = wave * kNPerWave + i;
-      float x = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) x += o_lds[w][row][16 * n + col];
-      dst[16 * n + col] = x * inv;
-    }
-    if (wave == 0 && col == 0) {
-      exp_sums[sh * max_parts + part] = Lsum[r];
-      max_logits[sh * max_parts + part] = M[r];
+    for (int n = 0; n < 8; ++n) dst[16 * n + col] = o[n][r] * inv;
+    if (col == 0) {
+      exp_sums[sh * max_parts + part] = l_run[r];
+      max_logits[sh * max_parts + part] = m_run[r];
     }
   }
 }
@@ -362,7 +423,7 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
   for (int32_t b = 0; b < nparts; b += kWave) {
     const int32_t p = b + lane;
     float wl = 0.0f;
-    if (p < nparts && es[p] > 0.0f) wl = es[p] * __expf(ml[p] - M);
+    if (p < nparts && es[p] > 0.0f) wl = es[p] * __builtin_amdgcn_exp2f(ml[p] - M);
     W += wl;
     const int cnt = nparts - b < kWave ? nparts - b : kWave;
     // every partition row below nparts was written by this call, with
@@ -398,39 +459,15 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
 int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t stream) {
   const int32_t P = a.partition_size;
   const int32_t max_parts = (a.max_context_len + P - 1) / P;
-  const int64_t units = (int64_t)a.num_seqs * a.num_kv_heads * max_parts;
+  const int64_t groups = (a.num_kv_heads + kPaWaves - 1) / kPaWaves;
+  const int64_t units = (int64_t)a.num_seqs * max_parts * groups;
   if (units > 0) {
-    const dim3 grid((unsigned)units);
-    switch (P) {
-      case 64:
-        hipLaunchKernelGGL(paged_attention_partition_kernel<1>, grid, dim3(kWave), 0, stream,
-                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
-                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
-                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
-                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
-        break;
-      case 128:
-        hipLaunchKernelGGL(paged_attention_partition_kernel<2>, grid, dim3(2 * kWave), 0, stream,
-                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
-                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
-                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
-                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
-        break;
-      case 256:
-        hipLaunchKernelGGL(paged_attention_partition_kernel<4>, grid, dim3(4 * kWave), 0, stream,
-                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
-                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
-                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
-                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
-        break;
-      default:
-        hipLaunchKernelGGL(paged_attention_partition_kernel<8>, grid, dim3(8 * kWave), 0, stream,
-                           a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
-                           a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
-                           a.num_kv_heads, a.block_size, a.max_blocks_per_seq, max_parts,
-                           a.num_blocks, a.scale, a.k_scale, a.v_scale);
-        break;
-    }
+    hipLaunchKernelGGL(paged_attention_partition_kernel, dim3((unsigned)units), dim3(kPaThreads), 0,
+                       stream, a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+                       a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
+                       a.num_kv_heads, a.block_size, FastDiv::make((uint32_t)a.block_size),
+                       a.max_blocks_per_seq, max_parts, P, a.num_blocks, a.scale, a.k_scale,
+                       a.v_scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }

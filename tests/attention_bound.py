@@ -10,12 +10,16 @@ W = sum_t w_t, o = sum_t w_t v_t / W:
    one multiply by fl(scale * k_scale): two more roundings.  We take
        delta_t = 2^-15 * s * sum_d |q_d c_d| + 2^-21 * |l_t|,  s = scale*k_scale
    (4x the accumulation bound).
-2. Exponentials.  Each token's weight passes through two hardware exp2
-   calls (inside its partition, then partition to global maximum), each
-   with relative error <= 2^-22 (1 + |x|) for argument x; |x| is at most
-   the logit range R of the row.  Together with 1., the device weights are
-   w_t (1 + g_t) with |g_t| <= gamma = max_t expm1(2 delta_t) +
-   2^-20 (1 + R) (the factor 2 on delta covers the shifted maximum).
+2. Exponentials.  Logits are scaled by log2(e) (in binary32) and each
+   weight is a product of hardware exp2 values: the token's own (against a
+   reference point that trails the running maximum by at most 2^8), up to
+   one rescale factor per 64-token block of its partition (at most 8), and
+   the partition's weight in the final combination.  Each has relative
+   error <= 2^-23 + 2^-24 |x| for an argument x of natural size; the |x|
+   along one product sum to at most 3 (R + 8 ln 2), with R the logit range
+   of the row.  Together with 1., the device weights are w_t (1 + g_t) with
+   |g_t| <= gamma = max_t expm1(2 delta_t) + 2^-18 (1 + R) (the factor 2 on
+   delta covers the shifted reference).
    Perturbing the weights moves the result by at most
        gamma / (1 - gamma) * C,   C = sum_t w_t |v_t - o| / W.
 3. The P.V product and the sums.  Probabilities enter the bf16 MFMA as a
@@ -86,7 +90,7 @@ def attention_bound(query_bits, key_cache, value_cache, block_tables, context_le
                 C = np.einsum("gt,gtd->gd", w, np.abs(Vh[None, :, :] - o[:, None, :])) / W
                 delta = 2.0 ** -15 * absdot + 2.0 ** -21 * np.abs(l)
                 R = l.max(1) - l.min(1)
-                gamma = (np.expm1(2 * delta).max(1) + 2.0 ** -20 * (1 + R))[:, None]
+                gamma = (np.expm1(2 * delta).max(1) + 2.0 ** -18 * (1 + R))[:, None]
                 alpha = beta = 2.0 ** -14
                 E = gamma * C / (1 - gamma) + (alpha * A * (1 + gamma) +
                                                beta * (np.abs(o) + gamma * C)) / (1 - beta)
