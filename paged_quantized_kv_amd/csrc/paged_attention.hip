@@ -11,25 +11,29 @@
 //   v_t = E4M3dec(value_cache[page][kvh][d][t%B]) * v_scale,
 //   page = block_tables[s][t/B], kvh = h / (num_heads / num_kv_heads).
 //
-// Partition kernel: one workgroup per (sequence, kv head, partition of
-// partition_size tokens), partition_size / 64 waves of 64 tokens each.  The
-// G = num_heads/num_kv_heads query heads of the kv head are the 16 rows of
-// v_mfma_f32_16x16x32_bf16 operands (rows >= G are zero); fp8 keys and values
-// become bf16 exactly (4 significant bits fit in 8).  A wave first issues
-// every load it needs -- two 16-byte key rows and eight 16-byte value rows
-// per lane, 16 KB per wave -- so that its whole share of the pages is in
-// flight at once, then computes.  The contractions run in the order those
-// loads deliver: over d, chunk c takes d = 16 (grp + 4 (c/2)) + 8 (c%2) + e
-// (the query operand is loaded in the same order); over tokens, the k index
-// 8 grp + e of MFMA h is token 16 grp + 8 h + e.  Per 16-token tile (inside
-// one page: block_size is a multiple of 16) 4 MFMAs give the 16 x 16 logits;
-// after the wave's max and exp-sum per head, the probabilities go through a
-// wave-private LDS slice (to operand order) as a bf16 high part plus the bf16
-// of the exact remainder (16 significant bits), and 4 MFMAs per 16 values of
-// d give the 16 x 128 partial output.  The waves then meet in LDS: common
-// maximum, rescaled exp-sums, summed outputs; the workgroup writes the
-// partition's normalised output, exp-sum and maximum to the caller's
-// workspace (exp_sums, max_logits, tmp_out), as the page's schema does.
+// Partition kernel: one wave per (sequence, kv head, partition of
+// partition_size tokens); a workgroup holds the waves of four consecutive kv
+// heads of one (sequence, partition).  The G = num_heads/num_kv_heads query
+// heads of the kv head are the 16 rows of v_mfma_f32_16x16x32_bf16 operands
+// (rows >= G are zero); fp8 keys and values become bf16 exactly (4
+// significant bits fit in 8).  The wave walks its partition in blocks of 64
+// tokens: per block each lane issues two 16-byte key rows and eight 16-byte
+// value rows (16 KB per wave), and the next block's keys are requested as
+// soon as the logits are formed, its values as soon as the P.V product has
+// consumed the current ones, so one block is always in flight.  The
+// contractions run in the order those loads deliver: over d, chunk c takes
+// d = 16 (grp + 4 (c/2)) + 8 (c%2) + e (the query operand is loaded in the
+// same order); over tokens, the k index 8 grp + e of MFMA h is token
+// 16 grp + 8 h + e.  Per 16-token tile (inside one page: block_size is a
+// multiple of 16) 4 MFMAs give the 16 x 16 logits; a running softmax (row
+// maxima and sums by DPP within 16-lane rows, exponentials as exp2 of logits
+// kept in log2(e) units, a reference point that moves only when a block
+// exceeds it by more than 2^8) turns them into weights, which go through a
+// wave-private LDS slice (to operand order) as a bf16 high part plus the
+// bf16 of the exact remainder (16 significant bits); 4 MFMAs per 16 values
+// of d give the 16 x 128 partial output.  The wave writes the partition's
+// normalised output, exp-sum and maximum to the caller's workspace
+// (exp_sums, max_logits, tmp_out), as the page's schema does.
 //
 // Reduce kernel: one wave per (sequence, head) combines the partitions:
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
