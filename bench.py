@@ -268,11 +268,12 @@ def time_decode_attention(args, pkv, torch, timing, stream, workloads, np):
     q = to(c.query.view(np.int16)).view(torch.bfloat16)
     kc, vc, bt, cl = to(c.key_cache), to(c.value_cache), to(c.block_tables), to(c.context_lens)
     out = torch.empty((S, H, D), dtype=torch.bfloat16, device="cuda")
-    ws = pkv.paged_attention_workspace(S, H, maxc, 256, device="cuda")
+    P = workloads.DECODE_PARTITION
+    ws = pkv.paged_attention_workspace(S, H, maxc, P, device="cuda")
 
     def call():
         pkv.pkv_paged_attention_decode(out, *ws, q, kc, vc, c.num_kv_heads, c.scale, bt, cl, B,
-                                       maxc, c.k_scale, c.v_scale, partition_size=256)
+                                       maxc, c.k_scale, c.v_scale, partition_size=P)
 
     evs = [[timing.create() for _ in range(2)] for _ in range(args.decode_steps)]
     for _ in range(min(args.warmup, 20)):
@@ -292,7 +293,7 @@ def time_decode_attention(args, pkv, torch, timing, stream, workloads, np):
             "seqs_per_s": round(S / (ms * 1e-3), 1),
             "context_tokens": int(c.context_lens.sum()),
             "workload": "decode step: 200 req, H=64, KVH=8, D=128, B=16, contexts U[128, 2560], "
-                        "fp8 E4M3 K/V, partitions of 256",
+                        f"fp8 E4M3 K/V, partitions of {P}",
             "traffic": measured_traffic("paged_attention_decode", "decode_200req")}
 
 

@@ -353,7 +353,7 @@ int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void *k,
  *   context_lens int32 [num_seqs].
  *   head_size 128; block_size a positive multiple of 16;
  *   num_heads a multiple of num_kv_heads with at most 16 query heads per KV
- *   head; partition_size 64, 128, 256 or 512; max_context_len <= 2^30;
+ *   head; partition_size a power of two in [64, 2048]; max_context_len <= 2^30;
  *   num_seqs*num_heads and num_seqs*num_kv_heads*max_num_partitions below
  *   2^31; scale, k_scale, v_scale finite host values.
  * The workspace is the caller's: the library allocates nothing.  Calls that

@@ -337,9 +337,9 @@ int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, fl
   if (block_size <= 0 || block_size % 16 != 0)
     return fail(PKV_EUNSUPPORTED, "%s: block_size must be a positive multiple of 16, got %d", op,
                 block_size);
-  if (partition_size != 64 && partition_size != 128 && partition_size != 256 && partition_size != 512)
-    return fail(PKV_EUNSUPPORTED, "%s: partition_size must be 64, 128, 256 or 512, got %d", op,
-                partition_size);
+  if (partition_size < 64 || partition_size > 2048 || (partition_size & (partition_size - 1)) != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: partition_size must be a power of two in [64, 2048], got %d",
+                op, partition_size);
   if (max_blocks_per_seq < 0)
     return fail(PKV_EINVAL, "%s: max_blocks_per_seq must be >= 0, got %d", op, max_blocks_per_seq);
   if (max_context_len < 0)

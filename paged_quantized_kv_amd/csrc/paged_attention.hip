@@ -13,27 +13,27 @@
 //
 // Partition kernel: one wave per (sequence, kv head, partition of
 // partition_size tokens); a workgroup holds the waves of four consecutive kv
-// heads of one (sequence, partition).  The G = num_heads/num_kv_heads query
-// heads of the kv head are the 16 rows of v_mfma_f32_16x16x32_bf16 operands
-// (rows >= G are zero); fp8 keys and values become bf16 exactly (4
-// significant bits fit in 8).  The wave walks its partition in blocks of 64
-// tokens: per block each lane issues two 16-byte key rows and eight 16-byte
-// value rows (16 KB per wave), and the next block's keys are requested as
-// soon as the logits are formed, its values as soon as the P.V product has
-// consumed the current ones, so one block is always in flight.  The
-// contractions run in the order those loads deliver: over d, chunk c takes
-// d = 16 (grp + 4 (c/2)) + 8 (c%2) + e (the query operand is loaded in the
-// same order); over tokens, the k index 8 grp + e of MFMA h is token
-// 16 grp + 8 h + e.  Per 16-token tile (inside one page: block_size is a
-// multiple of 16) 4 MFMAs give the 16 x 16 logits; a running softmax (row
-// maxima and sums by DPP within 16-lane rows, exponentials as exp2 of logits
-// kept in log2(e) units, a reference point that moves only when a block
-// exceeds it by more than 2^8) turns them into weights, which go through a
-// wave-private LDS slice (to operand order) as a bf16 high part plus the
-// bf16 of the exact remainder (16 significant bits); 4 MFMAs per 16 values
-// of d give the 16 x 128 partial output.  The wave writes the partition's
-// normalised output, exp-sum and maximum to the caller's workspace
-// (exp_sums, max_logits, tmp_out), as the page's schema does.
+// heads of one (sequence, partition).  Both products are computed
+// transposed, S^T = K Q^T and O^T = V^T P^T, on v_mfma_f32_16x16x32_bf16:
+// the 16 tokens of an MFMA's rows are chosen so that the logits a lane holds
+// afterwards are exactly the probabilities its B operand needs in P.V, so
+// the probabilities never leave registers, and each lane owns one query
+// head (the G = num_heads/num_kv_heads heads of the kv head are the 16
+// columns; columns >= G are zero).  fp8 keys and values become bf16 exactly
+// (4 significant bits fit in 8).  The wave walks its partition in blocks of
+// 64 tokens: per block each lane issues eight 16-byte key rows and eight
+// 16-byte value rows (16 KB per wave), and the next block's keys are
+// requested as soon as the logits are formed, its values as soon as the P.V
+// product has consumed the current ones.  A running softmax per head (the
+// maximum reduced over the four lane groups with the gfx950 lane-swap
+// instructions, exponentials as exp2 of logits kept in log2(e) units, a
+// reference point that moves only when a block exceeds it by more than 2^8)
+// turns logits into weights, which enter P.V as a bf16 high part plus the
+// bf16 of the exact remainder (16 significant bits).  The partition's
+// block-table entries are read once per wave into two registers and looked
+// up with v_readlane, so the loop issues no scalar loads.  The wave writes
+// the partition's normalised output, exp-sum and maximum to the caller's
+// workspace (exp_sums, max_logits, tmp_out), as the page's schema does.
 //
 // Reduce kernel: one wave per (sequence, head) combines the partitions:
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
@@ -77,103 +77,148 @@ __device__ __forceinline__ v8bf fp8x8_to_bf16(u32x2 w) {
   return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Lane exchange inside rows of 16 lanes by DPP (no LDS round trip).
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, false));
-}
-// Max / sum over the 16 lanes of each row: swap neighbours, swap pairs
-// (quad permutations), then the mirrored lane of the half row and of the
-// row, which pairs up the quads and then the halves.
-constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
-constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
-constexpr int kDppHalfMirror = 0x141; // row_half_mirror
-constexpr int kDppMirror = 0x140;     // row_mirror
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp<kDppXor1>(v));
-  v = fmaxf(v, dpp<kDppXor2>(v));
-  v = fmaxf(v, dpp<kDppHalfMirror>(v));
-  return fmaxf(v, dpp<kDppMirror>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp<kDppXor1>(v);
-  v += dpp<kDppXor2>(v);
-  v += dpp<kDppHalfMirror>(v);
-  return v + dpp<kDppMirror>(v);
-}
-
 __device__ __forceinline__ uint16_t bf16_rn(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Pages of the four 16-token tiles of the 64-token block starting at token
-// tb: table entries read without branches (column clamped into the row), so
-// that the four scalar reads are in flight together.
-struct BlockTable {
-  int32_t e[kPaTiles];
+// The block-table entries a partition can touch, two per lane: entry
+// j0 + lane in .lo and j0 + 64 + lane in .hi, -1 where the column is past the
+// row or the page id is outside [0, num_blocks).  A partition of at most 2048
+// tokens in pages of at least 16 spans at most 128 entries.  Loaded once per
+// wave with vector loads, so that the block loop issues no scalar loads.
+struct TableSlice {
+  int32_t lo, hi;
 };
-
-__device__ __forceinline__ BlockTable read_block_table(const int32_t* trow, int32_t max_blocks,
-                                                       const FastDiv& bdiv, int32_t tb) {
-  BlockTable t;
-  const int32_t jmax = max_blocks > 0 ? max_blocks - 1 : 0;
-#pragma unroll
-  for (int tt = 0; tt < kPaTiles; ++tt) {
-    const int32_t j = (int32_t)bdiv.div((uint32_t)(tb + tt * 16));
-    t.e[tt] = max_blocks > 0 ? trow[j < jmax ? j : jmax] : -1;
-  }
-  return t;
+__device__ __forceinline__ int32_t table_entry(const int32_t* trow, int32_t j,
+                                               int32_t max_blocks, int64_t num_blocks) {
+  const int32_t pg = j < max_blocks ? trow[j] : -1;
+  return (pg >= 0 && pg < num_blocks) ? pg : -1;
+}
+__device__ __forceinline__ TableSlice load_table_slice(const int32_t* trow, int32_t j0,
+                                                       int32_t max_blocks, int64_t num_blocks,
+                                                       int lane) {
+  return TableSlice{table_entry(trow, j0 + lane, max_blocks, num_blocks),
+                    table_entry(trow, j0 + kWave + lane, max_blocks, num_blocks)};
 }
 
-// Valid page id of each tile, or -1 (tile past the context, column past the
-// row, id outside [0, num_blocks)).
-__device__ __forceinline__ void block_pages(const BlockTable& t, int32_t tb, int32_t t_end,
-                                            int32_t max_blocks, const FastDiv& bdiv,
-                                            int64_t num_blocks, int32_t (&page)[kPaTiles]) {
+// Valid page id of each 16-token tile of the 64-token block starting at
+// token tb, or -1 (tile past the context, column past the row, invalid id).
+__device__ __forceinline__ void block_pages(const TableSlice& slice, int32_t j0, int32_t tb,
+                                            int32_t t_end, const FastDiv& bdiv,
+                                            int32_t (&page)[kPaTiles]) {
 #pragma unroll
   for (int tt = 0; tt < kPaTiles; ++tt) {
     const int32_t t0 = tb + tt * 16;
-    const int32_t j = (int32_t)bdiv.div((uint32_t)t0);
-    const int32_t pg = t.e[tt];
-    page[tt] = (t0 < t_end && j < max_blocks && pg >= 0 && pg < num_blocks) ? pg : -1;
+    const int32_t j = (int32_t)bdiv.div((uint32_t)(t0 < t_end ? t0 : tb)) - j0;
+    const int32_t pg = j < kWave ? __builtin_amdgcn_readlane(slice.lo, j)
+                                 : __builtin_amdgcn_readlane(slice.hi, j - kWave);
+    page[tt] = t0 < t_end ? pg : -1;
   }
+}
+
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four lane groups), by the
+// gfx950 lane-swap instructions: after a swap of the odd and even 16-lane rows
+// (then of the two halves) between two copies of v, each lane holds its own
+// value and its partner's.
+__device__ __forceinline__ float group4_max(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(v, fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+  const uint32_t w = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1])));
+}
+
+// 8 floats -> bf16 high parts (round to nearest even) and the bf16 of the
+// exact remainders, as MFMA operands; element k keeps position k.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ void split_bf16x8(const float (&p)[8], v8bf& hi, v8bf& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    h[k] = pack_bf16x2(p[2 * k], p[2 * k + 1]);
+    // p - hi is exact in binary32 (at most 16 significant bits remain)
+    l[k] = pack_bf16x2(p[2 * k] - __uint_as_float(h[k] << 16),
+                       p[2 * k + 1] - __uint_as_float(h[k] & 0xffff0000u));
+  }
+  hi = __builtin_bit_cast(v8bf, u32x4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(v8bf, u32x4{l[0], l[1], l[2], l[3]});
+}
+
+// One of four uniform values, chosen by a per-lane index in [0, 4): a select
+// chain on the values as scalars (readfirstlane makes them opaque, so the
+// selects cannot become an indexed access to the array, which would put the
+// array and everything around it in scratch memory).
+__device__ __forceinline__ int32_t pick4(const int32_t (&v)[kPaTiles], int idx) {
+  const int32_t v0 = __builtin_amdgcn_readfirstlane(v[0]);
+  const int32_t v1 = __builtin_amdgcn_readfirstlane(v[1]);
+  const int32_t v2 = __builtin_amdgcn_readfirstlane(v[2]);
+  const int32_t v3 = __builtin_amdgcn_readfirstlane(v[3]);
+  const int32_t lo = (idx & 1) ? v1 : v0;
+  const int32_t hi = (idx & 1) ? v3 : v2;
+  return (idx & 2) ? hi : lo;
 }
 
 // One wave per (sequence, kv head, partition); a workgroup holds the waves of
 // four consecutive kv heads of one (sequence, partition), so that all of
-// them have work or none has.  There is no barrier: waves only share the
-// workgroup's LDS through disjoint slices.
-__global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
-    float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
+// them have work or none has.  Waves share nothing: there is no barrier and
+// no LDS.
+//
+// Both products are computed transposed, S^T = K Q^T and O^T = V^T P^T, with
+// lane (col, grp) = (lane % 16, lane / 16):
+//  - logits, MFMA m of a 64-token block (m = 0..3): A row i is token
+//    16 (i/4) + 4m + i%4 (tile i/4 of the block), B column j is query head j
+//    of the group; the result gives lane (col, grp) the logits of head col for
+//    tokens 16 grp + 4m + r, r = 0..3 -- all in tile grp;
+//  - P.V, step s of a block (s = 0, 1): the K index 8 grp + e is token
+//    16 grp + 8s + e, so the B operand of lane (col, grp) is exactly the 8
+//    probabilities it holds from logits MFMAs 2s and 2s+1, and the A operand
+//    (values of d = 16n + col) is bytes 8s..8s+7 of tile grp's row d, one
+//    half of the 16-byte row the lane loads;
+//  - the result gives lane (col, grp) head col at d = 16n + 4 grp + r.
+// Each lane therefore owns one head: its running maximum is a scalar
+// (reduced over the four lane groups once per block) and its exp-sum a
+// per-lane partial, reduced at the end.
+// kB: the page size when it is fixed at compile time (all load offsets are
+// then immediates, which keeps the two stages within the register budget of
+// two waves per SIMD), 0 for any multiple of 16 given at run time.
+template <int kB>
+__device__ __forceinline__ void partition_unit(
+    uint32_t unit, float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
     const uint16_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t block_size, FastDiv bdiv, int32_t max_blocks, int32_t max_parts,
-    int32_t partition_size, int64_t num_blocks, float scale, float k_scale, float v_scale) {
-  constexpr int kPRow = kPaWaveTokens + 8;  // u16 per probability row
-  __shared__ __align__(16) uint16_t p_lds[kPaWaves][2][16][kPRow];
-
+    int32_t num_kv_heads, int32_t block_size_arg, FastDiv bdiv, int32_t max_blocks,
+    int32_t max_parts, int32_t partition_size, int64_t num_blocks, float scale, float k_scale,
+    float v_scale) {
+  const int32_t block_size = kB ? kB : block_size_arg;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
-  const int col = lane & 15;  // operand row / result column
-  const int grp = lane >> 4;  // K quarter / result row quarter
-  // 32-bit index arithmetic: the host bounds the grid and every token index
-  // below 2^31.  Partition-major order: the workgroups of all sequences'
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  // 32-bit index arithmetic: the host bounds the unit count and every token
+  // index below 2^31.  Partition-major order: the units of all sequences'
   // first partitions come first.
   const uint32_t groups = ((uint32_t)num_kv_heads + kPaWaves - 1) / kPaWaves;
-  const uint32_t unit = blockIdx.x;
   const uint32_t kvh = (unit % groups) * kPaWaves + wave;
   const uint32_t sp = unit / groups;
   const uint32_t s = sp % (uint32_t)num_seqs;
   const uint32_t part = sp / (uint32_t)num_seqs;
   if (kvh >= (uint32_t)num_kv_heads || part >= (uint32_t)max_parts) return;
-  const int32_t L = context_lens[s];
   const int32_t t_begin = (int32_t)part * partition_size;
+  const int32_t* trow = block_tables + (int64_t)s * max_blocks;
+  // the table slice does not depend on the context length: both are in
+  // flight together
+  const int32_t j0 = (int32_t)bdiv.div((uint32_t)t_begin);
+  const TableSlice slice = load_table_slice(trow, j0, max_blocks, num_blocks, lane);
+  const int32_t L = context_lens[s];
   if (t_begin >= L) return;
   const int32_t t_end = (L - t_begin > partition_size) ? t_begin + partition_size : L;
   const int32_t nblk = (t_end - t_begin + kPaWaveTokens - 1) / kPaWaveTokens;
   const int32_t G = num_heads / num_kv_heads;
-  const int32_t* trow = block_tables + (int64_t)s * max_blocks;
   const int64_t kv_head_keys = (int64_t)(kPaD / 16) * block_size * 16;  // bytes per (page, kv head)
   const int64_t kv_head_vals = (int64_t)kPaD * block_size;
   const uint8_t* kbase = key_cache + (int64_t)kvh * kv_head_keys;
@@ -181,9 +226,10 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
   const int64_t kpage = (int64_t)num_kv_heads * kv_head_keys;  // bytes per page, all kv heads
   const int64_t vpage = (int64_t)num_kv_heads * kv_head_vals;
 
-  // ---- query rows: chunk c of the contraction takes d = 16 (grp + 4 (c/2)) +
-  // 8 (c%2) + e, the order in which one 16-byte key row feeds it.  Rows past
-  // the group read the group's last head and are zeroed when used.
+  // ---- query operand (B of the logits): lane (col, grp) holds head col at
+  // d = 16 (grp + 4 (c/2)) + 8 (c%2) + e for K step c, the order in which one
+  // 16-byte key row feeds it.  Columns past the group read the group's last
+  // head and are zeroed.
   const uint16_t* qrow =
       query + ((int64_t)s * num_heads + (int64_t)kvh * G + (col < G ? col : G - 1)) * kPaD;
   u32x4 qv[4];
@@ -191,65 +237,53 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
   for (int c = 0; c < 4; ++c)
     qv[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * (grp + 4 * (c >> 1)) + 8 * (c & 1));
 
-  // Loads of one 64-token block.  Keys: lane (col, grp) holds rows grp and
-  // grp + 4 of token col of each tile.  Values: the 16 tokens of tile grp for
-  // d = 16n + col.  Tiles without a valid page read page 0 (in bounds) and
-  // are masked when used.
-  u32x4 kw[kPaTiles][2];
+  // Loads of one 64-token block.  Keys: for logits MFMA m, lane (col, grp)
+  // holds the 16-byte key rows grp and grp + 4 of token 16 (col/4) + 4m +
+  // col%4.  Values: the 16 tokens of tile grp at d = 16n + col.  Tiles
+  // without a valid page read page 0 (in bounds) and are masked when used.
+  u32x4 kw[4][2];
   u32x4 vw[8];
   auto issue_keys = [&](const int32_t (&pg)[kPaTiles], int32_t tb) {
+    const int32_t p = pick4(pg, col >> 2);
+    const uint32_t t0 = (uint32_t)(tb + (col >> 2) * 16);
+    const uint32_t off0 = t0 - bdiv.div(t0) * (uint32_t)block_size;
+    const uint8_t* kp = kbase + (int64_t)(p >= 0 ? p : 0) * kpage +
+                        ((int64_t)grp * block_size + off0 + (col & 3)) * 16;
 #pragma unroll
-    for (int tt = 0; tt < kPaTiles; ++tt) {
-      const uint32_t t0 = (uint32_t)(tb + tt * 16);
-      const int32_t off0 = (int32_t)(t0 - bdiv.div(t0) * (uint32_t)block_size);
-      const uint8_t* kp = kbase + (int64_t)(pg[tt] >= 0 ? pg[tt] : 0) * kpage;
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        kw[tt][h] = *reinterpret_cast<const u32x4*>(
-            kp + ((int64_t)(grp + 4 * h) * block_size + off0 + col) * 16);
-    }
-  };
-  // page of tile grp, by masks: a select chain on grp would be turned into an
-  // indexed (scratch) access to the array
-  const uint32_t sel0 = 0u - (uint32_t)(grp == 0), sel1 = 0u - (uint32_t)(grp == 1);
-  const uint32_t sel2 = 0u - (uint32_t)(grp == 2), sel3 = 0u - (uint32_t)(grp == 3);
-  auto lane_page = [&](const int32_t (&pg)[kPaTiles]) {
-    return (int32_t)(((uint32_t)pg[0] & sel0) | ((uint32_t)pg[1] & sel1) |
-                     ((uint32_t)pg[2] & sel2) | ((uint32_t)pg[3] & sel3));
+        kw[m][h] = *reinterpret_cast<const u32x4*>(kp + ((int64_t)4 * h * block_size + 4 * m) * 16);
   };
   auto issue_values = [&](const int32_t (&pg)[kPaTiles], int32_t tb) {
-    const int32_t pv = lane_page(pg);
+    const int32_t p = pick4(pg, grp);
     const uint32_t t0 = (uint32_t)(tb + grp * 16);
-    const uint8_t* vp = vbase + (int64_t)(pv >= 0 ? pv : 0) * vpage +
-                        (t0 - bdiv.div(t0) * (uint32_t)block_size);
+    const uint8_t* vp = vbase + (int64_t)(p >= 0 ? p : 0) * vpage +
+                        (t0 - bdiv.div(t0) * (uint32_t)block_size) + (int64_t)col * block_size;
 #pragma unroll
     for (int n = 0; n < 8; ++n)
-      vw[n] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * n + col) * block_size);
+      vw[n] = *reinterpret_cast<const u32x4*>(vp + (int64_t)16 * n * block_size);
   };
 
-  // ---- prologue: block 0's pages and loads; block 1's table entries
+  // ---- prologue: block 0's pages and loads
   int32_t page[kPaTiles];
-  {
-    const BlockTable t0 = read_block_table(trow, max_blocks, bdiv, t_begin);
-    block_pages(t0, t_begin, t_end, max_blocks, bdiv, num_blocks, page);
-  }
+  block_pages(slice, j0, t_begin, t_end, bdiv, page);
   issue_keys(page, t_begin);
   issue_values(page, t_begin);
-  BlockTable next_tbl = read_block_table(trow, max_blocks, bdiv, t_begin + kPaWaveTokens);
   __builtin_amdgcn_sched_barrier(0);  // block 0 is requested before anything waits
 
-  v8bf aq[4];
+  v8bf bq[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    aq[c] = __builtin_bit_cast(v8bf, col < G ? qv[c] : zero);
+    bq[c] = __builtin_bit_cast(v8bf, col < G ? qv[c] : zero);
   }
 
   // logits in units of log2(e), so that each weight is one hardware exp2
   const float qk_scale = (scale * k_scale) * kLog2e;
   const float neg_inf = -__builtin_inff();
-  float m_run[4] = {neg_inf, neg_inf, neg_inf, neg_inf};
-  float l_run[4] = {0.f, 0.f, 0.f, 0.f};
+  float m_run = neg_inf;  // reference point of head col
+  float l_part = 0.0f;    // exp-sum of head col over this lane's tokens
   v4f o[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) o[n] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -262,140 +296,148 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_partition_kernel(
   auto block = [&](int32_t b, auto prefetch) {
     constexpr bool kPrefetch = decltype(prefetch)::value;
     const int32_t tb = t_begin + b * kPaWaveTokens;
-    BlockTable tbl2;
-    if constexpr (kPrefetch)  // table entries two blocks ahead
-      tbl2 = read_block_table(trow, max_blocks, bdiv, tb + 2 * kPaWaveTokens);
+    // every token of the block is inside the context and has a valid page
+    const bool full = tb + kPaWaveTokens <= t_end && page[0] >= 0 && page[1] >= 0 &&
+                      page[2] >= 0 && page[3] >= 0;
 
-    // ---- logits of the block: lane holds token col of each tile, heads 4*grp + r
-    float lg[kPaTiles][4];
+    // ---- logits: lg[m][r] is head col at token 16 grp + 4m + r.  Each
+    // tile's four K steps run back to back on one accumulator, which the
+    // compiler then updates in place.  (With the K step outermost it gave the
+    // four chains separate source and destination accumulators and reused a
+    // source register for a conversion a few instructions after the MFMA that
+    // reads it, and the results were wrong at random.)
+    v4f acc[4];
 #pragma unroll
-    for (int tt = 0; tt < kPaTiles; ++tt) {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const u32x4 w = kw[tt][c >> 1];
+        const u32x4 w = kw[m][c >> 1];
         const u32x2 half = (c & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
-        acc = mfma_bf16(aq[c], fp8x8_to_bf16(half), acc);
+        acc[m] = mfma_bf16(fp8x8_to_bf16(half), bq[c], acc[m]);
       }
-      const bool valid = page[tt] >= 0 && tb + tt * 16 + col < t_end;
-      lg[tt][0] = valid ? acc.x * qk_scale : neg_inf;
-      lg[tt][1] = valid ? acc.y * qk_scale : neg_inf;
-      lg[tt][2] = valid ? acc.z * qk_scale : neg_inf;
-      lg[tt][3] = valid ? acc.w * qk_scale : neg_inf;
+    float lg[4][4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      lg[m][0] = acc[m].x * qk_scale;
+      lg[m][1] = acc[m].y * qk_scale;
+      lg[m][2] = acc[m].z * qk_scale;
+      lg[m][3] = acc[m].w * qk_scale;
+    }
+    const int32_t live = full ? kPaWaveTokens
+                              : (pick4(page, grp) >= 0 ? t_end - (tb + grp * 16) : 0);
+    if (!full) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * m + r >= live) lg[m][r] = neg_inf;
     }
     int32_t next_page[kPaTiles];
     if constexpr (kPrefetch) {
-      block_pages(next_tbl, tb + kPaWaveTokens, t_end, max_blocks, bdiv, num_blocks, next_page);
+      block_pages(slice, j0, tb + kPaWaveTokens, t_end, bdiv, next_page);
       issue_keys(next_page, tb + kPaWaveTokens);
     }
 
-    // ---- softmax reference point per head.  It only moves when the block's
-    // maximum exceeds it by more than 2^kLazy (weights stay <= 2^kLazy), so
-    // the output and exp-sum so far are rarely rescaled; the result is the
-    // same sum with other intermediate scalings.
-    float m_blk[4];
-    bool move = false;
+    // ---- softmax reference point of head col.  It only moves when the
+    // block's maximum exceeds it by more than 2^kLazy (weights stay <=
+    // 2^kLazy), so the output and exp-sum so far are rarely rescaled; the
+    // result is the same sum with other intermediate scalings.
+    float mx = neg_inf;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float v = neg_inf;
-#pragma unroll
-      for (int tt = 0; tt < kPaTiles; ++tt) v = fmaxf(v, lg[tt][r]);
-      m_blk[r] = row16_max(v);
-      move |= m_blk[r] > m_run[r] + kLazy;
-    }
+    for (int m = 0; m < 4; ++m)
+      mx = fmaxf(fmaxf(mx, fmaxf(lg[m][0], lg[m][1])), fmaxf(lg[m][2], lg[m][3]));
+    mx = group4_max(mx);
+    const bool move = mx > m_run + kLazy;
     if (__builtin_amdgcn_ballot_w64(move) != 0) {  // uniform over the wave
+      const float m_new = move ? mx : m_run;
+      const float alpha = (m_run == neg_inf) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_part *= alpha;
+      m_run = m_new;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) o[n] *= alpha;
+    }
+    float e = 0.0f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float m_new = m_blk[r] > m_run[r] + kLazy ? m_blk[r] : m_run[r];
-        const float alpha =
-            (m_run[r] == neg_inf) ? 0.0f : __builtin_amdgcn_exp2f(m_run[r] - m_new);
-        l_run[r] *= alpha;
-        m_run[r] = m_new;
-#pragma unroll
-        for (int n = 0; n < 8; ++n) o[n][r] *= alpha;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float e = 0.0f;
-#pragma unroll
-      for (int tt = 0; tt < kPaTiles; ++tt) {
-        const float p = (m_run[r] == neg_inf) ? 0.0f : __builtin_amdgcn_exp2f(lg[tt][r] - m_run[r]);
-        lg[tt][r] = p;
+        const float p = (m_run == neg_inf) ? 0.0f : __builtin_amdgcn_exp2f(lg[m][r] - m_run);
+        lg[m][r] = p;
         e += p;
       }
-      l_run[r] += row16_sum(e);
-    }
+    l_part += e;
 
-    // ---- probabilities to operand order through the wave's LDS slice, as a
-    // bf16 high part and the bf16 of the (exact) remainder
+    // ---- P.V: value bytes of tokens without a valid page or past the
+    // context are zeroed (the page may hold anything there)
+    if (!full) {
+      u32x4 keep;
 #pragma unroll
-    for (int tt = 0; tt < kPaTiles; ++tt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = lg[tt][r];
-        const uint16_t hi = bf16_rn(p);
-        p_lds[wave][0][4 * grp + r][16 * tt + col] = hi;
-        p_lds[wave][1][4 * grp + r][16 * tt + col] =
-            bf16_rn(p - __uint_as_float((uint32_t)hi << 16));
+      for (int q = 0; q < 4; ++q) {
+        const int32_t n_live = live - 4 * q;
+        keep[q] = n_live >= 4 ? 0xFFFFFFFFu : n_live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - n_live)));
       }
-    }
-    wave_sync();
-    // MFMA h of a d block takes K index 8*grp + e as token 16*grp + 8*h + e:
-    // probabilities from LDS, values from byte 8*h + e of the lane's 16.
-    v8bf ap[2][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int x = 0; x < 2; ++x)
-        ap[h][x] = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const u32x4*>(&p_lds[wave][x][col][16 * grp + 8 * h]));
-    wave_sync();  // the next block rewrites the slice
-
-    // value bytes of tokens without a valid page or past the context: zero
-    const int32_t live = lane_page(page) >= 0 ? t_end - (tb + grp * 16) : 0;
-    u32x4 keep;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int32_t n_live = live - 4 * q;
-      keep[q] = n_live >= 4 ? 0xFFFFFFFFu : n_live <= 0 ? 0u : (0xFFFFFFFFu >> (8 * (4 - n_live)));
+      for (int n = 0; n < 8; ++n) vw[n] &= keep;
     }
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const u32x4 w = vw[n] & keep;
-      const v8bf b0 = fp8x8_to_bf16(u32x2{w.x, w.y});
-      const v8bf b1 = fp8x8_to_bf16(u32x2{w.z, w.w});
-      o[n] = mfma_bf16(ap[0][0], b0, o[n]);
-      o[n] = mfma_bf16(ap[0][1], b0, o[n]);
-      o[n] = mfma_bf16(ap[1][0], b1, o[n]);
-      o[n] = mfma_bf16(ap[1][1], b1, o[n]);
+    for (int sp2 = 0; sp2 < 2; ++sp2) {
+      const float p8[8] = {lg[2 * sp2][0],     lg[2 * sp2][1],     lg[2 * sp2][2],
+                           lg[2 * sp2][3],     lg[2 * sp2 + 1][0], lg[2 * sp2 + 1][1],
+                           lg[2 * sp2 + 1][2], lg[2 * sp2 + 1][3]};
+      v8bf bhi, blo;
+      split_bf16x8(p8, bhi, blo);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const u32x4 w = vw[n];
+        const v8bf a = fp8x8_to_bf16(sp2 ? u32x2{w.z, w.w} : u32x2{w.x, w.y});
+        o[n] = mfma_bf16(a, bhi, o[n]);
+        o[n] = mfma_bf16(a, blo, o[n]);
+      }
     }
     if constexpr (kPrefetch) {
       __builtin_amdgcn_sched_barrier(0);  // the values are used before they are replaced
       issue_values(next_page, tb + kPaWaveTokens);
 #pragma unroll
       for (int tt = 0; tt < kPaTiles; ++tt) page[tt] = next_page[tt];
-      next_tbl = tbl2;
     }
   };
   for (int32_t b = 0; b + 1 < nblk; ++b) block(b, std::true_type{});
   block(nblk - 1, std::false_type{});
 
   // ---- normalised partial output, exp-sum and maximum of each real head
+  float l_run = l_part;
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (col < G) {
+    const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + col;
+    const float inv = l_run > 0.0f ? v_scale / l_run : 0.0f;
+    float* dst = tmp_out + (sh * max_parts + part) * kPaD + 4 * grp;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * grp + r;
-    if (row >= G) continue;
-    const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + row;
-    const float inv = l_run[r] > 0.0f ? v_scale / l_run[r] : 0.0f;
-    float* dst = tmp_out + (sh * max_parts + part) * kPaD;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) dst[16 * n + col] = o[n][r] * inv;
-    if (col == 0) {
-      exp_sums[sh * max_parts + part] = l_run[r];
-      max_logits[sh * max_parts + part] = m_run[r];
+    for (int n = 0; n < 8; ++n) *reinterpret_cast<v4f*>(dst + 16 * n) = o[n] * inv;
+    if (grp == 0) {
+      exp_sums[sh * max_parts + part] = l_run;
+      max_logits[sh * max_parts + part] = m_run;
     }
   }
+}
+
+// One workgroup per unit.
+template <int kB>
+__global__ __launch_bounds__(kPaThreads, 3) void paged_attention_partition_kernel(
+    uint32_t num_units, float* __restrict__ exp_sums, float* __restrict__ max_logits,
+    float* __restrict__ tmp_out, const uint16_t* __restrict__ query,
+    const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t block_size_arg,
+    FastDiv bdiv, int32_t max_blocks, int32_t max_parts, int32_t partition_size,
+    int64_t num_blocks, float scale, float k_scale, float v_scale) {
+  if (blockIdx.x < num_units)
+    partition_unit<kB>(blockIdx.x, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+                       block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
+                       block_size_arg, bdiv, max_blocks, max_parts, partition_size, num_blocks,
+                       scale, k_scale, v_scale);
 }
 
 // One wave per (sequence, head): lanes take the partitions' exp-sums and
@@ -466,8 +508,10 @@ int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t strea
   const int64_t groups = (a.num_kv_heads + kPaWaves - 1) / kPaWaves;
   const int64_t units = (int64_t)a.num_seqs * max_parts * groups;
   if (units > 0) {
-    hipLaunchKernelGGL(paged_attention_partition_kernel, dim3((unsigned)units), dim3(kPaThreads), 0,
-                       stream, a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+    auto kernel = a.block_size == 16 ? paged_attention_partition_kernel<16>
+                                     : paged_attention_partition_kernel<0>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kPaThreads), 0, stream,
+                       (uint32_t)units, a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
                        a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
                        a.num_kv_heads, a.block_size, FastDiv::make((uint32_t)a.block_size),
                        a.max_blocks_per_seq, max_parts, P, a.num_blocks, a.scale, a.k_scale,

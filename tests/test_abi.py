@@ -258,7 +258,8 @@ def pa(**kw):
     (dict(B=8), PKV_EUNSUPPORTED, "multiple of 16"),
     (dict(B=0), PKV_EUNSUPPORTED, "multiple of 16"),
     (dict(P=32), PKV_EUNSUPPORTED, "partition_size"),
-    (dict(P=1024), PKV_EUNSUPPORTED, "partition_size"),
+    (dict(P=4096), PKV_EUNSUPPORTED, "partition_size"),
+    (dict(P=384), PKV_EUNSUPPORTED, "partition_size"),
     (dict(maxc=(1 << 30) + 1), PKV_EUNSUPPORTED, "max_context_len"),
     (dict(S=1 << 25, H=128, KVH=8), PKV_EUNSUPPORTED, "below 2^31"),
     (dict(maxb=-1), PKV_EINVAL, "max_blocks_per_seq"),

@@ -83,12 +83,12 @@ def test_shapes(H, KVH, B, P):
 
 
 def test_long_contexts_many_partitions():
-    banner("paged attention long contexts, P=64 and 512")
+    banner("paged attention long contexts, P=64 to 2048")
     lens = [4100, 3000, 2049]
     c = workloads.paged_attention_case(9, len(lens), 16, 2, lens=lens)
     ref, b = reference(c)
-    check(run(c, 64), ref, b)
-    check(run(c, 512), ref, b)
+    for P in (64, 512, 1024, 2048):
+        check(run(c, P), ref, b)
 
 
 def test_edges_empty_invalid_pages_and_stale_bytes():
@@ -127,12 +127,12 @@ def test_repeated_calls_share_a_workspace_on_a_side_stream():
 
 def test_decode_batch_sampled():
     """The decode batch at its full size, in the launch configuration that is
-    timed (200 sequences, Llama-3.1-70B heads, 16-token pages, partitions of
-    256); the oracle checks a sample of sequences that includes the longest
+    timed (200 sequences, Llama-3.1-70B heads, 16-token pages, the bench's
+    partition size); the oracle checks a sample of sequences that includes the longest
     and the shortest."""
     banner("paged attention decode batch, sampled rows")
     c = workloads.decode_batch()
-    got = run(c, 256)
+    got = run(c, workloads.DECODE_PARTITION)
     L = c.context_lens
     rows = sorted({int(np.argmax(L)), int(np.argmin(L)), *range(0, len(L), 23)})
     ref, b = reference(c, rows)

@@ -381,6 +381,10 @@ def paged_attention_case(seed, num_seqs, num_heads, num_kv_heads, block_size=16,
 DECODE_SEQS = 200
 DECODE_HEADS, DECODE_KV_HEADS, DECODE_HEAD_SIZE, DECODE_BLOCK = 64, 8, 128, 16
 DECODE_MIN_CONTEXT, DECODE_MAX_CONTEXT = 128, 2560
+# Tokens per partition of the decode batch's attention calls.  The page's
+# kernel uses 256; the value only splits the work (results differ by rounding
+# within the error bound), and 1024 is the fastest split for this batch here.
+DECODE_PARTITION = 1024
 
 
 def decode_batch(seed=2024):
