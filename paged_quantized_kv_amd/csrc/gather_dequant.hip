@@ -264,6 +264,116 @@ __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_kernel(
   }
 }
 
+// Staged variant (head_size 64, 128 or 256, page sides of at most 16 KB,
+// 16-byte aligned): a wave first copies its whole page side -- every head's
+// codes and block scales, H*B*(D/2 + D/16) contiguous bytes -- into its LDS
+// slice with 16-byte loads that write LDS directly (global_load_lds_dwordx4:
+// lane i's 16 bytes land at the instruction's LDS base + 16 i, no registers
+// held), then produces the same units in the same order, reading each unit's
+// code dword and scale byte from LDS.  The 4- and 1-byte global loads of the
+// direct kernel become whole-line loads; bytes of the page past the run are
+// read but not used.
+constexpr int kFp4StageMax = 16384;  // bytes of one page side, at most
+constexpr int kFp4EmitUnroll = 4;    // units per lane in flight while emitting
+
+template <int kD, bool kF16, int kChunks>  // kChunks: 16-byte loads per lane, at most
+__global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_staged_kernel(
+    const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
+    uint16_t* __restrict__ key_out, int64_t key_row_stride, uint16_t* __restrict__ value_out,
+    int64_t value_row_stride, const int32_t* __restrict__ block_table,
+    const int32_t* __restrict__ cu_seq_lens, int32_t num_reqs, int32_t max_blocks,
+    int64_t num_tokens, int32_t num_heads, int32_t block_size, int64_t num_blocks,
+    int64_t page_stride, int32_t layout, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, FastDiv upt_div, int32_t side_bytes) {
+  extern __shared__ __align__(16) uint8_t stage_lds[];  // [kDqWaves][side_bytes]
+  constexpr int S = kD / 16;       // blocks (scale bytes) per token head
+  constexpr int hpt = kD / 8;      // half-blocks per token head
+  constexpr int data_dim = kD / 2;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  uint8_t* stage = stage_lds + (int64_t)wave * side_bytes;
+  const float ts_k = *k_scale, ts_v = *v_scale;
+  const int32_t upt = num_heads * hpt;  // half-blocks per token (upt_div divides by it)
+  const int32_t data_per_side = num_heads * block_size * data_dim;
+  const int32_t chunks = side_bytes / 16;
+  const int64_t units_total = (int64_t)num_reqs * max_blocks * 2;
+  const int64_t stride = (int64_t)gridDim.x * kDqWaves;
+  for (int64_t w = (int64_t)blockIdx.x * kDqWaves + threadIdx.x / kWave; w < units_total;
+       w += stride) {
+    const int64_t e = w >> 1;
+    const int kv = (int)(w & 1);
+    Run run;
+    if (!table_entry_run(block_table, cu_seq_lens, e, max_blocks, num_tokens, num_blocks,
+                         block_size, run))
+      continue;
+    // ---- the page side into LDS: chunk q = lane + 64 i lands at stage + 16 q.
+    // The previous unit's LDS reads have all returned (their values were
+    // stored), so the slice can be overwritten.
+    const u32x4* side =
+        reinterpret_cast<const u32x4*>((kv ? value_cache : key_cache) + run.page * page_stride);
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int q = lane + kWave * i;
+      if (q < chunks)
+        __builtin_amdgcn_global_load_lds(side + q, (__attribute__((address_space(3))) void*)(stage + i * kWave * 16), 16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has written LDS
+    wave_sync();
+
+    // ---- units in output order, from LDS
+    const uint8_t* scales = stage + data_per_side;
+    uint16_t* orow = (kv ? value_out : key_out) + run.row * (kv ? value_row_stride : key_row_stride);
+    const int64_t out_stride = kv ? value_row_stride : key_row_stride;
+    const float ts = kv ? ts_v : ts_k;
+    const int32_t units = (int32_t)run.rows * upt;
+    for (int32_t c0 = 0; c0 < units; c0 += kWave * kFp4EmitUnroll) {
+      uint32_t v[kFp4EmitUnroll], sb[kFp4EmitUnroll];
+#pragma unroll
+      for (int u = 0; u < kFp4EmitUnroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        v[u] = 0u;
+        sb[u] = 0u;
+        if (c < units) {
+          const int32_t t = (int32_t)upt_div.div((uint32_t)c);
+          const int32_t r = c - t * upt;
+          const int32_t h = r / hpt;
+          const int32_t hb = r - h * hpt;  // half-block within the head
+          const int32_t g = hb >> 1;
+          const int32_t off = (int32_t)run.first + t;
+          const int32_t row = layout == PKV_LAYOUT_HND ? h * block_size + off : off * num_heads + h;
+          v[u] = *reinterpret_cast<const uint32_t*>(stage + row * data_dim + hb * 4);
+          int32_t so;
+          if (kv == 0) {
+            so = row * S + g;
+          } else {
+            // swizzled: (t', s') = ((off/4)*4 + g/(S/4), (g % (S/4))*4 + off%4)
+            const int32_t gq = g / (S / 4);
+            const int32_t gr = g - gq * (S / 4);
+            const int32_t srow = (off >> 2) * 4 + gq;
+            const int32_t col = gr * 4 + (off & 3);
+            so = (layout == PKV_LAYOUT_HND ? (h * block_size + srow) * S
+                                           : (srow * num_heads + h) * S) + col;
+          }
+          sb[u] = scales[so];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kFp4EmitUnroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        if (c >= units) continue;
+        const int32_t t = (int32_t)upt_div.div((uint32_t)c);
+        const float sfd = __builtin_amdgcn_cvt_f32_fp8((int)sb[u], 0);
+        const u32x4 o = {fp4_pair<0, kF16>(v[u], sfd, ts), fp4_pair<1, kF16>(v[u], sfd, ts),
+                         fp4_pair<2, kF16>(v[u], sfd, ts), fp4_pair<3, kF16>(v[u], sfd, ts)};
+        store_stream(reinterpret_cast<u32x4*>(orow + (int64_t)t * out_stride +
+                                              (int64_t)(c - t * upt) * 8),
+                     o);
+      }
+    }
+  }
+}
+
 // Diagnostic: the output rounding of both gathers applied elementwise.
 template <bool kF16>
 __global__ __launch_bounds__(kDqThreads) void diag_narrow_kernel(const float* __restrict__ x,
@@ -301,9 +411,43 @@ int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stre
   return (int)hipGetLastError();
 }
 
+template <int kD, bool kF16>
+int launch_fp4_staged(const GatherFp4DequantArgs& a, int64_t units, int32_t side_bytes,
+                      hipStream_t stream) {
+  const int chunks = (side_bytes / 16 + kWave - 1) / kWave;  // 16-byte loads per lane
+  auto kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 16>;
+  if (chunks <= 4) kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 4>;
+  else if (chunks <= 8) kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 8>;
+  else if (chunks <= 12) kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 12>;
+  const uint32_t upt = (uint32_t)(a.num_heads * (kD / 8));
+  hipLaunchKernelGGL(kernel, dim3((unsigned)dq_blocks(units)), dim3(kDqThreads),
+                     (size_t)kDqWaves * side_bytes, stream, a.key_cache, a.value_cache, a.key_out,
+                     a.key_row_stride, a.value_out, a.value_row_stride, a.block_table,
+                     a.cu_seq_lens, a.num_reqs, a.max_blocks_per_req, a.num_tokens, a.num_heads,
+                     a.block_size, a.num_blocks, a.page_stride, a.layout, a.k_scale, a.v_scale,
+                     FastDiv::make(upt), side_bytes);
+  return (int)hipGetLastError();
+}
+
 int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream) {
   const int64_t units = (int64_t)a.num_reqs * a.max_blocks_per_req * 2;
   const bool f16 = a.out_dtype == PKV_DTYPE_F16;
+  // staged kernel: whole page sides of at most kFp4StageMax bytes, 16-byte aligned
+  const int64_t side_bytes =
+      (int64_t)a.num_heads * a.block_size * (a.head_size / 2 + a.head_size / 16);
+  const bool aligned16 = ((uintptr_t)a.key_cache % 16) == 0 && ((uintptr_t)a.value_cache % 16) == 0 &&
+                         a.page_stride % 16 == 0 && side_bytes % 16 == 0;
+  if (aligned16 && side_bytes <= kFp4StageMax) {
+    switch (a.head_size) {
+      case 64: return f16 ? launch_fp4_staged<64, true>(a, units, (int32_t)side_bytes, stream)
+                          : launch_fp4_staged<64, false>(a, units, (int32_t)side_bytes, stream);
+      case 128: return f16 ? launch_fp4_staged<128, true>(a, units, (int32_t)side_bytes, stream)
+                           : launch_fp4_staged<128, false>(a, units, (int32_t)side_bytes, stream);
+      case 256: return f16 ? launch_fp4_staged<256, true>(a, units, (int32_t)side_bytes, stream)
+                           : launch_fp4_staged<256, false>(a, units, (int32_t)side_bytes, stream);
+      default: break;
+    }
+  }
   auto kernel = f16 ? gather_kv_fp4_dequant_kernel<0, true> : gather_kv_fp4_dequant_kernel<0, false>;
   if (a.head_size == 64) kernel = f16 ? gather_kv_fp4_dequant_kernel<64, true> : gather_kv_fp4_dequant_kernel<64, false>;
   if (a.head_size == 128) kernel = f16 ? gather_kv_fp4_dequant_kernel<128, true> : gather_kv_fp4_dequant_kernel<128, false>;
