@@ -346,7 +346,7 @@ __global__ __launch_bounds__(kFp4Threads) void store_kv_fp4_kernel(
     const int64_t* __restrict__ slot_mapping, int64_t token0, uint32_t num_items,
     int32_t num_heads, int32_t head_size, int32_t block_size, int32_t log2_bs, int64_t num_blocks,
     int64_t page_stride, int32_t layout, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, Div halves, Div scale_dim, Div quarter_s) {
+    const float* __restrict__ v_scale, Div halves, Div scale_dim) {
   __shared__ float gs_over_m[2][16];  // RN(gs / M), M = 1..15, per side
   const GlobalScales G = load_global_scales(k_scale, v_scale, gs_over_m);
   const int32_t S = scale_dim.d;
@@ -455,7 +455,6 @@ int launch_generic(const StoreFp4Args& a, hipStream_t stream) {
   const int64_t halves = 2 * (int64_t)a.num_heads * S;  // half-blocks per token side
   const Div halves_div{(int32_t)halves, log2_exact(halves)};
   const Div scale_dim{S, log2_exact(S)};
-  const Div quarter_s{S / 4, log2_exact(S / 4)};
   // Items are indexed in 32 bits: split the tokens into launches of at most
   // 2^31 items each.
   const int64_t max_tokens = (int64_t{1} << 31) / (2 * halves);
@@ -470,7 +469,7 @@ int launch_generic(const StoreFp4Args& a, hipStream_t stream) {
                        a.key, a.key_row_stride, a.value, a.value_row_stride, a.key_cache,
                        a.value_cache, a.slot_mapping, t0, items, a.num_heads, a.head_size,
                        a.block_size, a.log2_block_size, a.num_blocks, a.page_stride, a.layout,
-                       a.k_scale, a.v_scale, halves_div, scale_dim, quarter_s);
+                       a.k_scale, a.v_scale, halves_div, scale_dim);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
   }
