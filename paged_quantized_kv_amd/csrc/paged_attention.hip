@@ -301,11 +301,9 @@ __device__ __forceinline__ void partition_unit(
                       page[2] >= 0 && page[3] >= 0;
 
     // ---- logits: lg[m][r] is head col at token 16 grp + 4m + r.  Each
-    // tile's four K steps run back to back on one accumulator, which the
-    // compiler then updates in place.  (With the K step outermost it gave the
-    // four chains separate source and destination accumulators and reused a
-    // source register for a conversion a few instructions after the MFMA that
-    // reads it, and the results were wrong at random.)
+    // tile's four K steps run back to back on one accumulator.  (With the K
+    // step as the outer loop, the same arithmetic gave wrong results that
+    // depended on timing; the cause was not found, so that order is not used.)
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
