@@ -166,6 +166,13 @@ def run_fp4_readback(f, cache_np, bt, cu, dtype="bf16", pad=0, guard=2, k_scale=
     ([200, 17, 33], 1, 256, 32, 1, "bf16", 0),
     ([48, 48, 13, 50], 4, 128, 12, 0, "f16", 16),
     ([300], 2, 512, 4, 0, "bf16", 0),
+    # page sides of 4608 and 16128 bytes (8 and 16 staged loads per lane),
+    # and two shapes the staged kernel leaves to the direct one: a side of
+    # 18432 bytes (over 16 KB) and head_size 192
+    ([33, 64], 4, 128, 16, 0, "bf16", 8),
+    ([70, 16, 5], 14, 128, 16, 1, "f16", 0),
+    ([70, 16, 5], 16, 128, 16, 0, "bf16", 0),
+    ([20, 9], 3, 192, 8, 1, "bf16", 0),
 ])
 def test_fp4_readback_paged(lens, H, D, B, layout, dtype, pad):
     banner(f"nvfp4 readback lens={lens} H={H} D={D} B={B} layout={layout} {dtype} pad={pad}")
