@@ -35,7 +35,11 @@
 // the partition's normalised output, exp-sum and maximum to the caller's
 // workspace (exp_sums, max_logits, tmp_out), as the page's schema does.
 //
-// Reduce kernel: one wave per (sequence, head) combines the partitions:
+// A sequence whose context fits one partition gets its output row from the
+// partition kernel directly (normalised, rounded to bf16).
+//
+// Reduce kernel: one wave per (sequence, head) of the other sequences
+// combines the partitions:
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
 // and rounds to bf16.  A sequence without a valid token gets a zero row;
 // tokens whose page id is outside [0, num_blocks) are left out.
@@ -187,7 +191,7 @@ __device__ __forceinline__ int32_t pick4(const int32_t (&v)[kPaTiles], int idx) 
 // two waves per SIMD), 0 for any multiple of 16 given at run time.
 template <int kB>
 __device__ __forceinline__ void partition_unit(
-    uint32_t unit, float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
+    uint32_t unit, uint16_t* __restrict__ out, float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
     const uint16_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
     const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
@@ -216,6 +220,9 @@ __device__ __forceinline__ void partition_unit(
   const TableSlice slice = load_table_slice(trow, j0, max_blocks, num_blocks, lane);
   const int32_t L = context_lens[s];
   if (t_begin >= L) return;
+  // partitions of this sequence (as the reduce kernel counts them)
+  const int32_t nparts = (L - 1) / partition_size + 1 < max_parts ? (L - 1) / partition_size + 1
+                                                                   : max_parts;
   const int32_t t_end = (L - t_begin > partition_size) ? t_begin + partition_size : L;
   const int32_t nblk = (t_end - t_begin + kPaWaveTokens - 1) / kPaWaveTokens;
   const int32_t G = num_heads / num_kv_heads;
@@ -404,11 +411,23 @@ __device__ __forceinline__ void partition_unit(
   for (int32_t b = 0; b + 1 < nblk; ++b) block(b, std::true_type{});
   block(nblk - 1, std::false_type{});
 
-  // ---- normalised partial output, exp-sum and maximum of each real head
+  // ---- normalised partial output, exp-sum and maximum of each real head;
+  // a sequence of one partition gets its output row here (the reduce kernel
+  // skips it)
   float l_run = l_part;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (col < G) {
+  if (col < G && nparts == 1) {
+    const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + col;
+    const float inv = l_run > 0.0f ? v_scale / l_run : 0.0f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const v4f v = o[n] * inv;
+      const u32x2 w = {(uint32_t)bf16_rn(v.x) | ((uint32_t)bf16_rn(v.y) << 16),
+                       (uint32_t)bf16_rn(v.z) | ((uint32_t)bf16_rn(v.w) << 16)};
+      *reinterpret_cast<u32x2*>(out + sh * kPaD + 16 * n + 4 * grp) = w;
+    }
+  } else if (col < G) {
     const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + col;
     const float inv = l_run > 0.0f ? v_scale / l_run : 0.0f;
     float* dst = tmp_out + (sh * max_parts + part) * kPaD + 4 * grp;
@@ -424,7 +443,7 @@ __device__ __forceinline__ void partition_unit(
 // One workgroup per unit.
 template <int kB>
 __global__ __launch_bounds__(kPaThreads, 3) void paged_attention_partition_kernel(
-    uint32_t num_units, float* __restrict__ exp_sums, float* __restrict__ max_logits,
+    uint32_t num_units, uint16_t* __restrict__ out, float* __restrict__ exp_sums, float* __restrict__ max_logits,
     float* __restrict__ tmp_out, const uint16_t* __restrict__ query,
     const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
@@ -432,7 +451,7 @@ __global__ __launch_bounds__(kPaThreads, 3) void paged_attention_partition_kerne
     FastDiv bdiv, int32_t max_blocks, int32_t max_parts, int32_t partition_size,
     int64_t num_blocks, float scale, float k_scale, float v_scale) {
   if (blockIdx.x < num_units)
-    partition_unit<kB>(blockIdx.x, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
+    partition_unit<kB>(blockIdx.x, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
                        block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
                        block_size_arg, bdiv, max_blocks, max_parts, partition_size, num_blocks,
                        scale, k_scale, v_scale);
@@ -452,6 +471,7 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
   const int32_t L = context_lens[s];
   int32_t nparts = L > 0 ? (L - 1) / partition_size + 1 : 0;
   if (nparts > max_parts) nparts = max_parts;
+  if (nparts == 1) return;  // the partition kernel wrote this row
   const float* es = exp_sums + (int64_t)sh * max_parts;
   const float* ml = max_logits + (int64_t)sh * max_parts;
   const float neg_inf = -__builtin_inff();
@@ -509,7 +529,7 @@ int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t strea
     auto kernel = a.block_size == 16 ? paged_attention_partition_kernel<16>
                                      : paged_attention_partition_kernel<0>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kPaThreads), 0, stream,
-                       (uint32_t)units, a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
+                       (uint32_t)units, a.out, a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
                        a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
                        a.num_kv_heads, a.block_size, FastDiv::make((uint32_t)a.block_size),
                        a.max_blocks_per_seq, max_parts, P, a.num_blocks, a.scale, a.k_scale,
