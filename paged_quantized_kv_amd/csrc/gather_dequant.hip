@@ -176,6 +176,84 @@ __global__ __launch_bounds__(kDqThreads) void gather_indexer_k_dequant_kernel(
   }
 }
 
+// Staged variant (runs of at most 64 tokens whose code rows fit 8 KB): the
+// wave first copies the run's code rows into its LDS slice with
+// global_load_lds_dwordx4 (all of them in flight at once, no registers
+// held), then produces the same units from LDS.  The direct kernel keeps a
+// few units' loads in flight and waits for them before every group of
+// stores.
+constexpr int kIdxStageMax = 8192;  // code bytes of one run, at most
+constexpr int kIdxStageChunks = kIdxStageMax / (16 * kWave);  // 16-byte loads per lane
+
+template <bool kF16>
+__global__ __launch_bounds__(kDqThreads) void gather_indexer_k_dequant_staged_kernel(
+    const uint8_t* __restrict__ kv_cache, uint16_t* __restrict__ out, int64_t out_row_stride,
+    const int32_t* __restrict__ block_table, const int32_t* __restrict__ cu_seq_lens,
+    int32_t num_reqs, int32_t max_blocks, int64_t num_tokens, int64_t num_blocks,
+    int64_t page_stride, int32_t block_size, int32_t head_dim, FastDiv upt_div) {
+  __shared__ __align__(16) uint8_t stage_lds[kDqWaves][kIdxStageMax];
+  const int lane = threadIdx.x & (kWave - 1);
+  uint8_t* stage = stage_lds[threadIdx.x / kWave];
+  const int64_t entries = (int64_t)num_reqs * max_blocks;
+  const int64_t stride = (int64_t)gridDim.x * kDqWaves;
+  const int32_t upt = head_dim / 8;  // 8-code units per token (upt_div divides by it)
+  for (int64_t e = (int64_t)blockIdx.x * kDqWaves + threadIdx.x / kWave; e < entries;
+       e += stride) {
+    Run run;
+    if (!table_entry_run(block_table, cu_seq_lens, e, max_blocks, num_tokens, num_blocks,
+                         block_size, run))
+      continue;
+    const uint8_t* page = kv_cache + run.page * page_stride;
+    const u32x4* csrc = reinterpret_cast<const u32x4*>(page + run.first * head_dim);
+    const float* ssrc =
+        reinterpret_cast<const float*>(page + (int64_t)block_size * head_dim) + run.first;
+    const int32_t chunks = (int32_t)run.rows * head_dim / 16;
+    // the previous run's LDS reads have all returned (their values were stored)
+    wave_sync();
+#pragma unroll
+    for (int i = 0; i < kIdxStageChunks; ++i) {
+      const int q = lane + kWave * i;
+      if (q < chunks)
+        __builtin_amdgcn_global_load_lds(csrc + q, (__attribute__((address_space(3))) void*)(stage + i * kWave * 16), 16, 0, 0);
+    }
+    // lane l holds the scale of token l (runs have at most 64 tokens)
+    const float my_scale = lane < run.rows ? ssrc[lane] : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has written LDS
+    wave_sync();
+
+    uint16_t* orow = out + run.row * out_row_stride;
+    const int32_t units = (int32_t)run.rows * upt;
+    for (int32_t c0 = 0; c0 < units; c0 += kWave * kIdxUnroll) {
+      u32x2 v[kIdxUnroll];
+      float sc[kIdxUnroll];
+#pragma unroll
+      for (int u = 0; u < kIdxUnroll; ++u) {  // every lane takes part (bpermute)
+        const int32_t c = c0 + u * kWave + lane;
+        const int32_t t = c < units ? (int32_t)upt_div.div((uint32_t)c) : 0;
+        v[u] = c < units ? *reinterpret_cast<const u32x2*>(stage + c * 8) : u32x2{0u, 0u};
+        sc[u] = __uint_as_float(
+            (uint32_t)__builtin_amdgcn_ds_bpermute(t << 2, (int)__float_as_uint(my_scale)));
+      }
+#pragma unroll
+      for (int u = 0; u < kIdxUnroll; ++u) {
+        const int32_t c = c0 + u * kWave + lane;
+        if (c >= units) continue;
+        const int32_t t = (int32_t)upt_div.div((uint32_t)c);
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].x, false);
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].x, true);
+        const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].y, false);
+        const f32x2 g = __builtin_amdgcn_cvt_pk_f32_fp8((int)v[u].y, true);
+        const float x = sc[u];
+        const u32x4 o = {narrow2<kF16>(a.x * x, a.y * x), narrow2<kF16>(b.x * x, b.y * x),
+                         narrow2<kF16>(d.x * x, d.y * x), narrow2<kF16>(g.x * x, g.y * x)};
+        store_stream(reinterpret_cast<u32x4*>(orow + (int64_t)t * out_row_stride +
+                                              (int64_t)(c - t * upt) * 8),
+                     o);
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------- NVFP4 K/V
 // Work of a wave: one (table entry, side) -- the run's tokens, every head.
 // Lane unit = one half-block (4 code bytes, 8 elements of one token head) ->
@@ -401,8 +479,13 @@ int64_t dq_blocks(int64_t units) {
 
 int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stream) {
   const int64_t entries = (int64_t)a.num_reqs * a.max_blocks_per_req;
-  auto kernel = a.out_dtype == PKV_DTYPE_F16 ? gather_indexer_k_dequant_kernel<true>
-                                             : gather_indexer_k_dequant_kernel<false>;
+  const bool f16 = a.out_dtype == PKV_DTYPE_F16;
+  // staged kernel: runs of at most 64 tokens, code rows of at most 8 KB
+  const bool staged = a.block_size <= kWave && (int64_t)a.block_size * a.head_dim <= kIdxStageMax;
+  auto kernel = staged ? (f16 ? gather_indexer_k_dequant_staged_kernel<true>
+                              : gather_indexer_k_dequant_staged_kernel<false>)
+                       : (f16 ? gather_indexer_k_dequant_kernel<true>
+                              : gather_indexer_k_dequant_kernel<false>);
   hipLaunchKernelGGL(kernel, dim3((unsigned)dq_blocks(entries)), dim3(kDqThreads), 0, stream,
                      a.kv_cache, a.out, a.out_row_stride, a.block_table, a.cu_seq_lens,
                      a.num_reqs, a.max_blocks_per_req, a.num_tokens, a.num_blocks,
