@@ -38,8 +38,8 @@
 // A sequence whose context fits one partition gets its output row from the
 // partition kernel directly (normalised, rounded to bf16).
 //
-// Reduce kernel: one wave per (sequence, head) of the other sequences
-// combines the partitions:
+// Reduce kernel: each (sequence, head) row of the other sequences combines
+// its partitions:
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
 // and rounds to bf16.  A sequence without a valid token gets a zero row;
 // tokens whose page id is outside [0, num_blocks) are left out.
@@ -457,65 +457,62 @@ __global__ __launch_bounds__(kPaThreads, 3) void paged_attention_partition_kerne
                        scale, k_scale, v_scale);
 }
 
-// One wave per (sequence, head): lanes take the partitions' exp-sums and
-// maxima in parallel, then the weighted partial outputs (two d per lane).
+// Eight (sequence, head) rows per wave: lane l takes row 8w + l/8 and the 16
+// values d = 16 (l%8) + i of it, and walks the row's partitions itself, so
+// the combination needs no lane exchange and the partial outputs are loaded
+// independently of the maxima.
+constexpr int kRdRowsPerWave = 8;
 __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ exp_sums,
     const float* __restrict__ max_logits, const float* __restrict__ tmp_out,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
     int32_t max_parts, int32_t partition_size) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t sh = blockIdx.x * kPaWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (sh >= (uint32_t)num_seqs * (uint32_t)num_heads) return;
-  const uint32_t s = sh / (uint32_t)num_heads;
-  const int32_t L = context_lens[s];
+  const uint32_t w = blockIdx.x * kPaWaves + threadIdx.x / kWave;
+  const uint32_t sh = w * kRdRowsPerWave + (uint32_t)(lane >> 3);
+  if (sh >= (uint32_t)num_seqs * (uint32_t)num_heads) return;  // no lane exchange below
+  const int sub = lane & 7;
+  const int32_t L = context_lens[sh / (uint32_t)num_heads];
   int32_t nparts = L > 0 ? (L - 1) / partition_size + 1 : 0;
   if (nparts > max_parts) nparts = max_parts;
   if (nparts == 1) return;  // the partition kernel wrote this row
   const float* es = exp_sums + (int64_t)sh * max_parts;
   const float* ml = max_logits + (int64_t)sh * max_parts;
+  const float* o = tmp_out + (int64_t)sh * max_parts * kPaD + 16 * sub;
   const float neg_inf = -__builtin_inff();
   float M = neg_inf;
-  for (int32_t b = 0; b < nparts; b += kWave) {
-    const int32_t p = b + lane;
-    if (p < nparts && es[p] > 0.0f) M = fmaxf(M, ml[p]);
-  }
+  for (int32_t p = 0; p < nparts; ++p)
+    if (es[p] > 0.0f) M = fmaxf(M, ml[p]);
+  // every partition row below nparts was written by this call with finite
+  // values, so rows of weight 0 add exactly 0
+  float W = 0.0f;
+  v4f acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                {0.f, 0.f, 0.f, 0.f}};
+  for (int32_t p = 0; p < nparts; ++p) {
+    const v4f* row = reinterpret_cast<const v4f*>(o + (int64_t)p * kPaD);
+    const v4f v0 = row[0], v1 = row[1], v2 = row[2], v3 = row[3];
+    const float wp = es[p] > 0.0f ? es[p] * __builtin_amdgcn_exp2f(ml[p] - M) : 0.0f;
+    W += wp;
+    const v4f v[4] = {v0, v1, v2, v3};
 #pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, __shfl_xor(M, d));
-  float W = 0.0f, a0 = 0.0f, a1 = 0.0f;
-  const float* o = tmp_out + (int64_t)sh * max_parts * kPaD + 2 * lane;
-  for (int32_t b = 0; b < nparts; b += kWave) {
-    const int32_t p = b + lane;
-    float wl = 0.0f;
-    if (p < nparts && es[p] > 0.0f) wl = es[p] * __builtin_amdgcn_exp2f(ml[p] - M);
-    W += wl;
-    const int cnt = nparts - b < kWave ? nparts - b : kWave;
-    // every partition row below nparts was written by this call, with
-    // finite values, so rows of weight 0 add exactly 0
-    int i = 0;
-    for (; i + 8 <= cnt; i += 8) {  // eight rows in flight
-      f32x2 v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x2*>(o + (int64_t)(b + i + u) * kPaD);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = __shfl(wl, i + u);
-        a0 = __builtin_fmaf(w, v[u].x, a0);
-        a1 = __builtin_fmaf(w, v[u].y, a1);
-      }
-    }
-    for (; i < cnt; ++i) {
-      const float w = __shfl(wl, i);
-      const f32x2 v = *reinterpret_cast<const f32x2*>(o + (int64_t)(b + i) * kPaD);
-      a0 = __builtin_fmaf(w, v.x, a0);
-      a1 = __builtin_fmaf(w, v.y, a1);
+    for (int i = 0; i < 4; ++i) {
+      acc[i].x = __builtin_fmaf(wp, v[i].x, acc[i].x);
+      acc[i].y = __builtin_fmaf(wp, v[i].y, acc[i].y);
+      acc[i].z = __builtin_fmaf(wp, v[i].z, acc[i].z);
+      acc[i].w = __builtin_fmaf(wp, v[i].w, acc[i].w);
     }
   }
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) W += __shfl_xor(W, d);
   const float inv = W > 0.0f ? 1.0f / W : 0.0f;
-  const uint32_t packed = (uint32_t)bf16_rn(a0 * inv) | ((uint32_t)bf16_rn(a1 * inv) << 16);
-  *reinterpret_cast<uint32_t*>(out + (int64_t)sh * kPaD + 2 * lane) = packed;
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v4f v = acc[i] * inv;
+    packed[2 * i] = (uint32_t)bf16_rn(v.x) | ((uint32_t)bf16_rn(v.y) << 16);
+    packed[2 * i + 1] = (uint32_t)bf16_rn(v.z) | ((uint32_t)bf16_rn(v.w) << 16);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(out + (int64_t)sh * kPaD + 16 * sub);
+  dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+  dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
 }
 
 }  // namespace
@@ -538,7 +535,8 @@ int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t strea
     if (e != hipSuccess) return (int)e;
   }
   const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-  hipLaunchKernelGGL(paged_attention_reduce_kernel, dim3((unsigned)((rows + kPaWaves - 1) / kPaWaves)),
+  const int64_t rows_per_block = (int64_t)kPaWaves * kRdRowsPerWave;
+  hipLaunchKernelGGL(paged_attention_reduce_kernel, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
                      dim3(kPaThreads), 0, stream, a.out, a.exp_sums, a.max_logits, a.tmp_out,
                      a.context_lens, a.num_seqs, a.num_heads, max_parts, P);
   return (int)hipGetLastError();
