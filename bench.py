@@ -33,11 +33,13 @@ head size 128, 16-token pages, contexts uniform in [128, 2560]: 0.5 GB of K/V
 codes), reported under `decode_attention`.
 
 Printed: one JSON line.  `value` = algorithmic bytes of one step / measured
-step time (GB/s); per-kernel durations come from HIP events recorded on the
-launch stream around each launch (timing-only events, without the cache
-write-back a default event performs); `roofline` describes the kernel with the
-longest average duration; `cpu_baseline` times the CPU oracle on the same
-batch (one thread).
+step time (GB/s), the wall clock of K steps with nothing between the
+launches; the per-kernel durations come from the K steps that follow, with
+HIP events recorded on the launch stream around each launch (timing-only
+events, without the cache write-back a default event performs), and
+`ms_per_step_with_events` is those steps' wall clock; `roofline` describes
+the kernel with the longest average duration; `cpu_baseline` times the CPU
+oracle on the same batch (one thread).
 """
 from __future__ import annotations
 
@@ -382,15 +384,24 @@ def main():
     # default warmup (~30 ms of steps) runs past the clock transient that the
     # first few dozen launches of the step show, so the timed steps measure the
     # sustained rate.
+    # The step's wall clock is taken over K steps with no event between
+    # launches (each recorded event is one more packet the command processor
+    # waits on, about 2 us per event here); the per-kernel durations come
+    # from the next K steps, with events around every launch.
     events = [[timing.create() for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, events[i])
+        step(args.warmup + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i, events[i])
+    torch.cuda.synchronize()
+    wall_events = time.perf_counter() - t1
 
     per_kernel_ms = {n: 0.0 for n in names}
     for ev in events:
@@ -456,6 +467,7 @@ def main():
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "mtokens_per_s": round(T / (ms_per_step * 1e-3) / 1e6, 2),
         "event_ms_per_step": round(sum(per_kernel_ms.values()), 4),
+        "ms_per_step_with_events": round(wall_events * 1e3 / args.steps, 4),
         "kernels": kernels,
         "roofline": roofline,
         "input_gen_s": round(t_gen, 1),
