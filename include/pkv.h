@@ -329,10 +329,17 @@ int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void *k,
  * zero row.  Only tokens t < ceil(max_context_len / partition_size) *
  * partition_size are read: max_context_len must be >= every context_lens[s].
  *
- * The work is split, as on the page, into partitions of partition_size
- * tokens: a first kernel writes each partition's softmax denominator,
- * maximum logit and normalised partial output to the caller's workspace,
- * and a second combines them.  The dot products run on bf16 MFMA
+ * The work is split into segments: runs of whole 64-token blocks of one
+ * sequence, at most 2048 tokens.  When the workspace has room, the blocks of
+ * all sequences are dealt out in equal shares, one per wave the GPU holds at
+ * once, so that mixed context lengths keep every wave equally busy; else
+ * (or for more than 4096 sequences) each partition of partition_size tokens
+ * is a segment, as on the page.  A first kernel writes each segment's
+ * softmax denominator, maximum logit and normalised partial output to the
+ * caller's workspace (a sequence that is a single segment gets its output
+ * row directly), and a second combines them.  partition_size therefore
+ * sizes the workspace and the fixed split; the result does not depend on it
+ * beyond rounding.  The dot products run on bf16 MFMA
  * (v_mfma_f32_16x16x32_bf16; fp8 keys and values are exact in bf16, the
  * probabilities enter as a bf16 high + low pair) with binary32
  * accumulation, and the exponentials on the hardware exp2; results agree

@@ -11,9 +11,15 @@
 //   v_t = E4M3dec(value_cache[page][kvh][d][t%B]) * v_scale,
 //   page = block_tables[s][t/B], kvh = h / (num_heads / num_kv_heads).
 //
-// Partition kernel: one wave per (sequence, kv head, partition of
-// partition_size tokens); a workgroup holds the waves of four consecutive kv
-// heads of one (sequence, partition).  Both products are computed
+// Partition kernel: one wave per (kv head, segment), a segment being a run
+// of whole 64-token blocks of one sequence; a workgroup holds the waves of
+// four consecutive kv heads.  The balanced split numbers the blocks of all
+// sequences in order and gives every unit of work the same count (so mixed
+// context lengths leave no wave with much more to do than the others); the
+// fixed split, as on the page, makes one segment per partition of
+// partition_size tokens and serves the batches the balanced one cannot
+// (one partition of workspace per sequence, very many sequences).  Both
+// products are computed
 // transposed, S^T = K Q^T and O^T = V^T P^T, on v_mfma_f32_16x16x32_bf16:
 // the 16 tokens of an MFMA's rows are chosen so that the logits a lane holds
 // afterwards are exactly the probabilities its B operand needs in P.V, so
@@ -29,17 +35,18 @@
 // instructions, exponentials as exp2 of logits kept in log2(e) units, a
 // reference point that moves only when a block exceeds it by more than 2^8)
 // turns logits into weights, which enter P.V as a bf16 high part plus the
-// bf16 of the exact remainder (16 significant bits).  The partition's
+// bf16 of the exact remainder (16 significant bits).  The segment's
 // block-table entries are read once per wave into two registers and looked
 // up with v_readlane, so the loop issues no scalar loads.  The wave writes
-// the partition's normalised output, exp-sum and maximum to the caller's
-// workspace (exp_sums, max_logits, tmp_out), as the page's schema does.
+// the segment's normalised output, exp-sum and maximum to the caller's
+// workspace (exp_sums, max_logits, tmp_out), the buffers of the page's
+// schema.
 //
-// A sequence whose context fits one partition gets its output row from the
+// A sequence whose context is a single segment gets its output row from the
 // partition kernel directly (normalised, rounded to bf16).
 //
 // Reduce kernel: each (sequence, head) row of the other sequences combines
-// its partitions:
+// its segments' partials:
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
 // and rounds to bf16.  A sequence without a valid token gets a zero row;
 // tokens whose page id is outside [0, num_blocks) are left out.
@@ -166,10 +173,10 @@ __device__ __forceinline__ int32_t pick4(const int32_t (&v)[kPaTiles], int idx) 
   return (idx & 2) ? hi : lo;
 }
 
-// One wave per (sequence, kv head, partition); a workgroup holds the waves of
-// four consecutive kv heads of one (sequence, partition), so that all of
-// them have work or none has.  Waves share nothing: there is no barrier and
-// no LDS.
+// One wave attends one kv head of one sequence over one segment of its
+// context: a run of whole 64-token blocks (the last one ragged), at most 2048
+// tokens, given by the work split (below).  Waves share nothing: there is
+// no barrier and no LDS.
 //
 // Both products are computed transposed, S^T = K Q^T and O^T = V^T P^T, with
 // lane (col, grp) = (lane % 16, lane / 16):
@@ -190,40 +197,17 @@ __device__ __forceinline__ int32_t pick4(const int32_t (&v)[kPaTiles], int idx) 
 // then immediates, which keeps the two stages within the register budget of
 // two waves per SIMD), 0 for any multiple of 16 given at run time.
 template <int kB>
-__device__ __forceinline__ void partition_unit(
-    uint32_t unit, uint16_t* __restrict__ out, float* __restrict__ exp_sums, float* __restrict__ max_logits, float* __restrict__ tmp_out,
-    const uint16_t* __restrict__ query, const uint8_t* __restrict__ key_cache,
-    const uint8_t* __restrict__ value_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t num_kv_heads, int32_t block_size_arg, FastDiv bdiv, int32_t max_blocks,
-    int32_t max_parts, int32_t partition_size, int64_t num_blocks, float scale, float k_scale,
-    float v_scale) {
+__device__ __forceinline__ void attend_segment(
+    uint32_t s, uint32_t kvh, int32_t t_begin, int32_t t_end, const TableSlice& slice, int32_t j0,
+    int64_t row, bool direct, uint16_t* __restrict__ out, float* __restrict__ exp_sums,
+    float* __restrict__ max_logits, float* __restrict__ tmp_out, const uint16_t* __restrict__ query,
+    const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
+    int32_t num_heads, int32_t num_kv_heads, int32_t block_size_arg, FastDiv bdiv, float scale,
+    float k_scale, float v_scale) {
   const int32_t block_size = kB ? kB : block_size_arg;
   const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
   const int col = lane & 15;
   const int grp = lane >> 4;
-  // 32-bit index arithmetic: the host bounds the unit count and every token
-  // index below 2^31.  Partition-major order: the units of all sequences'
-  // first partitions come first.
-  const uint32_t groups = ((uint32_t)num_kv_heads + kPaWaves - 1) / kPaWaves;
-  const uint32_t kvh = (unit % groups) * kPaWaves + wave;
-  const uint32_t sp = unit / groups;
-  const uint32_t s = sp % (uint32_t)num_seqs;
-  const uint32_t part = sp / (uint32_t)num_seqs;
-  if (kvh >= (uint32_t)num_kv_heads || part >= (uint32_t)max_parts) return;
-  const int32_t t_begin = (int32_t)part * partition_size;
-  const int32_t* trow = block_tables + (int64_t)s * max_blocks;
-  // the table slice does not depend on the context length: both are in
-  // flight together
-  const int32_t j0 = (int32_t)bdiv.div((uint32_t)t_begin);
-  const TableSlice slice = load_table_slice(trow, j0, max_blocks, num_blocks, lane);
-  const int32_t L = context_lens[s];
-  if (t_begin >= L) return;
-  // partitions of this sequence (as the reduce kernel counts them)
-  const int32_t nparts = (L - 1) / partition_size + 1 < max_parts ? (L - 1) / partition_size + 1
-                                                                   : max_parts;
-  const int32_t t_end = (L - t_begin > partition_size) ? t_begin + partition_size : L;
   const int32_t nblk = (t_end - t_begin + kPaWaveTokens - 1) / kPaWaveTokens;
   const int32_t G = num_heads / num_kv_heads;
   const int64_t kv_head_keys = (int64_t)(kPaD / 16) * block_size * 16;  // bytes per (page, kv head)
@@ -411,98 +395,292 @@ __device__ __forceinline__ void partition_unit(
   for (int32_t b = 0; b + 1 < nblk; ++b) block(b, std::true_type{});
   block(nblk - 1, std::false_type{});
 
-  // ---- normalised partial output, exp-sum and maximum of each real head;
-  // a sequence of one partition gets its output row here (the reduce kernel
-  // skips it)
+  // ---- normalised output of each real head: the output row itself when the
+  // segment is the sequence's whole context, else the segment's partial
+  // output, exp-sum and maximum for the reduce kernel
   float l_run = l_part;
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (col < G && nparts == 1) {
-    const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + col;
+  if (col < G) {
+    const int64_t h = (int64_t)kvh * G + col;
     const float inv = l_run > 0.0f ? v_scale / l_run : 0.0f;
+    if (direct) {
+      uint16_t* dst = out + ((int64_t)s * num_heads + h) * kPaD + 4 * grp;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const v4f v = o[n] * inv;
-      const u32x2 w = {(uint32_t)bf16_rn(v.x) | ((uint32_t)bf16_rn(v.y) << 16),
-                       (uint32_t)bf16_rn(v.z) | ((uint32_t)bf16_rn(v.w) << 16)};
-      *reinterpret_cast<u32x2*>(out + sh * kPaD + 16 * n + 4 * grp) = w;
-    }
-  } else if (col < G) {
-    const int64_t sh = (int64_t)s * num_heads + (int64_t)kvh * G + col;
-    const float inv = l_run > 0.0f ? v_scale / l_run : 0.0f;
-    float* dst = tmp_out + (sh * max_parts + part) * kPaD + 4 * grp;
+      for (int n = 0; n < 8; ++n) {
+        const v4f v = o[n] * inv;
+        const u32x2 w = {(uint32_t)bf16_rn(v.x) | ((uint32_t)bf16_rn(v.y) << 16),
+                         (uint32_t)bf16_rn(v.z) | ((uint32_t)bf16_rn(v.w) << 16)};
+        *reinterpret_cast<u32x2*>(dst + 16 * n) = w;
+      }
+    } else {
+      const int64_t e = row * num_heads + h;
+      float* dst = tmp_out + e * kPaD + 4 * grp;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) *reinterpret_cast<v4f*>(dst + 16 * n) = o[n] * inv;
-    if (grp == 0) {
-      exp_sums[sh * max_parts + part] = l_run;
-      max_logits[sh * max_parts + part] = m_run;
+      for (int n = 0; n < 8; ++n) *reinterpret_cast<v4f*>(dst + 16 * n) = o[n] * inv;
+      if (grp == 0) {
+        exp_sums[e] = l_run;
+        max_logits[e] = m_run;
+      }
     }
   }
 }
 
-// One workgroup per unit.
+// ---- Work split.
+//
+// Fixed split (as on the page): one workgroup per (sequence, partition of
+// partition_size tokens, four consecutive kv heads); partition p of
+// sequence s has workspace row s * max_parts + p.
 template <int kB>
 __global__ __launch_bounds__(kPaThreads, 3) void paged_attention_partition_kernel(
-    uint32_t num_units, uint16_t* __restrict__ out, float* __restrict__ exp_sums, float* __restrict__ max_logits,
-    float* __restrict__ tmp_out, const uint16_t* __restrict__ query,
+    uint32_t num_units, uint16_t* __restrict__ out, float* __restrict__ exp_sums,
+    float* __restrict__ max_logits, float* __restrict__ tmp_out, const uint16_t* __restrict__ query,
     const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t block_size_arg,
     FastDiv bdiv, int32_t max_blocks, int32_t max_parts, int32_t partition_size,
     int64_t num_blocks, float scale, float k_scale, float v_scale) {
-  if (blockIdx.x < num_units)
-    partition_unit<kB>(blockIdx.x, out, exp_sums, max_logits, tmp_out, query, key_cache, value_cache,
-                       block_tables, context_lens, num_seqs, num_heads, num_kv_heads,
-                       block_size_arg, bdiv, max_blocks, max_parts, partition_size, num_blocks,
-                       scale, k_scale, v_scale);
+  if (blockIdx.x >= num_units) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
+  // 32-bit index arithmetic: the host bounds the unit count and every token
+  // index below 2^31.  Partition-major order: the units of all sequences'
+  // first partitions come first.
+  const uint32_t groups = ((uint32_t)num_kv_heads + kPaWaves - 1) / kPaWaves;
+  const uint32_t kvh = (blockIdx.x % groups) * kPaWaves + wave;
+  const uint32_t sp = blockIdx.x / groups;
+  const uint32_t s = sp % (uint32_t)num_seqs;
+  const uint32_t part = sp / (uint32_t)num_seqs;
+  if (kvh >= (uint32_t)num_kv_heads || part >= (uint32_t)max_parts) return;
+  const int32_t t_begin = (int32_t)part * partition_size;
+  // the table slice does not depend on the context length: both are in
+  // flight together
+  const int32_t j0 = (int32_t)bdiv.div((uint32_t)t_begin);
+  const TableSlice slice =
+      load_table_slice(block_tables + (int64_t)s * max_blocks, j0, max_blocks, num_blocks, lane);
+  const int32_t L = context_lens[s];
+  if (t_begin >= L) return;
+  const int32_t nparts = (L - 1) / partition_size + 1 < max_parts ? (L - 1) / partition_size + 1
+                                                                   : max_parts;
+  const int32_t t_end = (L - t_begin > partition_size) ? t_begin + partition_size : L;
+  attend_segment<kB>(s, kvh, t_begin, t_end, slice, j0, (int64_t)s * max_parts + part,
+                     nparts == 1, out, exp_sums, max_logits, tmp_out, query, key_cache,
+                     value_cache, num_heads, num_kv_heads, block_size_arg, bdiv, scale, k_scale,
+                     v_scale);
 }
 
-// Eight (sequence, head) rows per wave: lane l takes row 8w + l/8 and the 16
-// values d = 16 (l%8) + i of it, and walks the row's partitions itself, so
-// the combination needs no lane exchange and the partial outputs are loaded
-// independently of the maxima.
-constexpr int kRdRowsPerWave = 8;
+// Balanced split.  With one partition per fixed number of tokens, a batch of
+// mixed context lengths gives some waves many more blocks than others, and
+// the call lasts as long as the longest.  Here the 64-token blocks of all
+// sequences are numbered in sequence order, block j of sequence s being
+// number cum(s) + j with cum(s) = sum over s' < s of blocks(s'), N in all,
+// and unit u of num_units takes numbers [u W, (u + 1) W), W = ceil(N /
+// num_units): every wave gets the same number of blocks, in one or more
+// segments (one per sequence its range touches).  Sequence s then has
+// partials from units first(s) = floor(cum(s) / W) through last(s) =
+// floor((cum(s) + blocks(s) - 1) / W); the partial of unit u goes to
+// workspace row u + s, which no other (unit, sequence) pair uses, since
+// last(s) <= first(s') for s < s', and rows stay below num_units +
+// num_seqs.  The wave of kv head 0 that attends the first block of a
+// sequence also records (first(s) + s, last(s) - first(s) + 1) for the
+// reduce kernel, as two int32 at exp_sums entries (num_units + num_seqs) *
+// num_heads + 2 s and + 1.  The host bounds num_units so that all of it fits
+// the caller's [num_seqs, num_heads, max_parts] workspace, and makes W at
+// most 32 blocks (2048 tokens, the table slice).  Tokens past token_cap =
+// max_parts * partition_size are not read, as in the fixed split.
+
+// 64-token blocks of a context of L tokens of which at most `cap` are read.
+__device__ __forceinline__ int32_t seq_blocks(int32_t L, int32_t cap) {
+  const int32_t n = L < cap ? L : cap;
+  return n > 0 ? (n + kPaWaveTokens - 1) / kPaWaveTokens : 0;
+}
+
+// Lane i sums the blocks of sequences [i per, (i + 1) per), per =
+// ceil(num_seqs / 64); base is the lane's exclusive prefix of those sums and
+// total (uniform) is N.  All lanes must be active.
+struct SeqPrefix {
+  int32_t per, base, total;
+};
+__device__ __forceinline__ SeqPrefix seq_prefix(const int32_t* __restrict__ context_lens,
+                                                int32_t num_seqs, int32_t cap, int lane) {
+  const int32_t per = (num_seqs + kWave - 1) / kWave;
+  const int32_t first = lane * per;
+  int32_t mine = 0;
+  for (int32_t k0 = 0; k0 < per; k0 += 8) {  // eight loads in flight per lane
+    int32_t L[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int32_t k = k0 + i;
+      L[i] = (k < per && first + k < num_seqs) ? context_lens[first + k] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) mine += seq_blocks(L[i], cap);
+  }
+  const int32_t incl = wave_inclusive_scan(mine);
+  return SeqPrefix{per, incl - mine, __builtin_amdgcn_readlane(incl, kWave - 1)};
+}
+
+// A workgroup per (unit, four consecutive kv heads).
+template <int kB>
+__global__ __launch_bounds__(kPaThreads, 3) void paged_attention_balanced_kernel(
+    uint32_t num_units, uint16_t* __restrict__ out, float* __restrict__ exp_sums,
+    float* __restrict__ max_logits, float* __restrict__ tmp_out, const uint16_t* __restrict__ query,
+    const uint8_t* __restrict__ key_cache, const uint8_t* __restrict__ value_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ context_lens,
+    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t block_size_arg,
+    FastDiv bdiv, int32_t max_blocks, int32_t token_cap, int64_t num_blocks, float scale,
+    float k_scale, float v_scale) {
+  const uint32_t groups = ((uint32_t)num_kv_heads + kPaWaves - 1) / kPaWaves;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // uniform per wave
+  const uint32_t u = blockIdx.x / groups;
+  const uint32_t kvh = (blockIdx.x % groups) * kPaWaves + wave;
+  if (u >= num_units || kvh >= (uint32_t)num_kv_heads) return;
+  const SeqPrefix pre = seq_prefix(context_lens, num_seqs, token_cap, lane);
+  const int32_t N = pre.total;
+  if (N == 0) return;
+  const int32_t W = (int32_t)(((int64_t)N + num_units - 1) / num_units);
+  const int64_t b0l = (int64_t)u * W;
+  if (b0l >= N) return;
+  const int32_t b0 = (int32_t)b0l;
+  const int32_t b1 = N - b0 > W ? b0 + W : N;
+
+  // first sequence with cum(s) + blocks(s) > b0: the lane range that holds
+  // it, then the sequence inside that range
+  int32_t s = 0, cum = 0;
+  {
+    // lane i's range ends at base_i + mine_i; mine_i = base_{i+1} - base_i
+    const int32_t end_i = __shfl_down(pre.base, 1);
+    const int32_t end = lane == kWave - 1 ? N : end_i;
+    const uint64_t m = __builtin_amdgcn_ballot_w64(end > b0);
+    const int32_t r = (int32_t)__builtin_ctzll(m);
+    const int32_t rbase = __builtin_amdgcn_readlane(pre.base, r);
+    const int32_t sq = r * pre.per + lane;
+    const int32_t nb = lane < pre.per && sq < num_seqs ? seq_blocks(context_lens[sq], token_cap) : 0;
+    const int32_t incl = wave_inclusive_scan(nb);
+    const int32_t k = (int32_t)__builtin_ctzll(
+        __builtin_amdgcn_ballot_w64(lane < pre.per && rbase + incl > b0));
+    s = r * pre.per + k;
+    cum = rbase + __builtin_amdgcn_readlane(incl, k) - __builtin_amdgcn_readlane(nb, k);
+  }
+
+  // the segments: sequences s, s + 1, ... while their blocks start below b1
+  while (cum < b1 && s < num_seqs) {
+    const int32_t lo = b0 > cum ? b0 - cum : 0;  // first block of the segment in s
+    const int32_t t_begin = lo * kPaWaveTokens;
+    const int32_t j0 = (int32_t)bdiv.div((uint32_t)t_begin);
+    const TableSlice slice =
+        load_table_slice(block_tables + (int64_t)s * max_blocks, j0, max_blocks, num_blocks, lane);
+    const int32_t Lraw = context_lens[s];
+    const int32_t L = Lraw < token_cap ? Lraw : token_cap;
+    const int32_t nb = seq_blocks(L, token_cap);
+    if (nb > 0) {
+      const int32_t hi = b1 - cum < nb ? b1 - cum : nb;  // end block of the segment in s
+      const int32_t t_end = hi * kPaWaveTokens < L ? hi * kPaWaveTokens : L;
+      const int32_t first = cum / W;
+      const int32_t count = (cum + nb - 1) / W - first + 1;
+      if (lo == 0 && kvh == 0 && lane == 0) {
+        int32_t* meta = reinterpret_cast<int32_t*>(exp_sums) +
+                        ((int64_t)num_units + num_seqs) * num_heads + 2 * (int64_t)s;
+        meta[0] = first + s;
+        meta[1] = count;
+      }
+      const bool direct = count == 1;
+      attend_segment<kB>(s, kvh, t_begin, t_end, slice, j0, (int64_t)u + s, direct, out,
+                         exp_sums, max_logits, tmp_out, query, key_cache, value_cache, num_heads,
+                         num_kv_heads, block_size_arg, bdiv, scale, k_scale, v_scale);
+    }
+    cum += nb;
+    ++s;
+  }
+}
+
+// ---- Reduce: one wave per (sequence, eight heads); lane l takes head
+// 8 g + l/8 and the 16 values d = 16 (l%8) + i of it, and walks the head's
+// partials itself, four at a time (their exp-sums, maxima and outputs all
+// loaded at once), so the combination needs no lane exchange.  Rows of one partial
+// (the partition kernel wrote them) are skipped; rows with no valid token
+// become zero.  num_units = 0 selects the fixed split.
 __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
     uint16_t* __restrict__ out, const float* __restrict__ exp_sums,
     const float* __restrict__ max_logits, const float* __restrict__ tmp_out,
     const int32_t* __restrict__ context_lens, int32_t num_seqs, int32_t num_heads,
-    int32_t max_parts, int32_t partition_size) {
+    int32_t max_parts, int32_t partition_size, uint32_t num_units, int32_t token_cap) {
   const int lane = threadIdx.x & (kWave - 1);
-  const uint32_t w = blockIdx.x * kPaWaves + threadIdx.x / kWave;
-  const uint32_t sh = w * kRdRowsPerWave + (uint32_t)(lane >> 3);
-  if (sh >= (uint32_t)num_seqs * (uint32_t)num_heads) return;  // no lane exchange below
+  const uint32_t hg = ((uint32_t)num_heads + 7) / 8;
+  const uint32_t w = blockIdx.x * kPaWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (w >= (uint32_t)num_seqs * hg) return;
+  const int32_t s = (int32_t)(w / hg);
+  const int32_t h = (int32_t)(w % hg) * 8 + (lane >> 3);
   const int sub = lane & 7;
-  const int32_t L = context_lens[sh / (uint32_t)num_heads];
-  int32_t nparts = L > 0 ? (L - 1) / partition_size + 1 : 0;
-  if (nparts > max_parts) nparts = max_parts;
-  if (nparts == 1) return;  // the partition kernel wrote this row
-  const float* es = exp_sums + (int64_t)sh * max_parts;
-  const float* ml = max_logits + (int64_t)sh * max_parts;
-  const float* o = tmp_out + (int64_t)sh * max_parts * kPaD + 16 * sub;
-  const float neg_inf = -__builtin_inff();
-  float M = neg_inf;
-  for (int32_t p = 0; p < nparts; ++p)
-    if (es[p] > 0.0f) M = fmaxf(M, ml[p]);
-  // every partition row below nparts was written by this call with finite
-  // values, so rows of weight 0 add exactly 0
-  float W = 0.0f;
-  v4f acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
-                {0.f, 0.f, 0.f, 0.f}};
-  for (int32_t p = 0; p < nparts; ++p) {
-    const v4f* row = reinterpret_cast<const v4f*>(o + (int64_t)p * kPaD);
-    const v4f v0 = row[0], v1 = row[1], v2 = row[2], v3 = row[3];
-    const float wp = es[p] > 0.0f ? es[p] * __builtin_amdgcn_exp2f(ml[p] - M) : 0.0f;
-    W += wp;
-    const v4f v[4] = {v0, v1, v2, v3};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i].x = __builtin_fmaf(wp, v[i].x, acc[i].x);
-      acc[i].y = __builtin_fmaf(wp, v[i].y, acc[i].y);
-      acc[i].z = __builtin_fmaf(wp, v[i].z, acc[i].z);
-      acc[i].w = __builtin_fmaf(wp, v[i].w, acc[i].w);
+  int64_t r0 = 0;
+  int32_t count = 0;
+  if (num_units == 0) {
+    const int32_t L = context_lens[s];
+    count = L > 0 ? (L - 1) / partition_size + 1 : 0;
+    if (count > max_parts) count = max_parts;
+    r0 = (int64_t)s * max_parts;
+  } else {
+    // the partition kernel recorded the sequence's rows (only for a
+    // sequence with blocks; anything else there is stale)
+    const int32_t* meta = reinterpret_cast<const int32_t*>(exp_sums) +
+                          ((int64_t)num_units + num_seqs) * num_heads + 2 * (int64_t)s;
+    const int32_t m0 = meta[0], m1 = meta[1];
+    if (seq_blocks(context_lens[s], token_cap) > 0 && m0 >= 0 && m1 >= 0 &&
+        (int64_t)m0 + m1 <= (int64_t)num_units + num_seqs) {
+      r0 = m0;
+      count = m1;
     }
   }
-  const float inv = W > 0.0f ? 1.0f / W : 0.0f;
+  if (count == 1) return;  // the partition kernel wrote this row
+  if (h >= num_heads) return;
+  // four partials at a time, all their loads in flight together; the
+  // running maximum M and the sums are rescaled when a group raises M
+  const float neg_inf = -__builtin_inff();
+  float M = neg_inf;
+  float Wsum = 0.0f;
+  v4f acc[4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f},
+                {0.f, 0.f, 0.f, 0.f}};
+  for (int32_t p0 = 0; p0 < count; p0 += 4) {
+    float es[4], ml[4];
+    v4f v[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool in = p0 + j < count;
+      const int64_t e = (r0 + (in ? p0 + j : 0)) * num_heads + h;
+      const v4f* row = reinterpret_cast<const v4f*>(tmp_out + e * kPaD + 16 * sub);
+      es[j] = in ? exp_sums[e] : 0.0f;
+      ml[j] = in ? max_logits[e] : neg_inf;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[j][i] = in ? row[i] : v4f{0.f, 0.f, 0.f, 0.f};
+    }
+    // every partial row read here was written by this call with finite
+    // values, so a partial of weight 0 adds exactly 0
+    float mg = M;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (es[j] > 0.0f) mg = fmaxf(mg, ml[j]);
+    if (mg > M) {
+      const float alpha = M == neg_inf ? 0.0f : __builtin_amdgcn_exp2f(M - mg);
+      Wsum *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= alpha;
+      M = mg;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float wp = es[j] > 0.0f ? es[j] * __builtin_amdgcn_exp2f(ml[j] - M) : 0.0f;
+      Wsum += wp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i].x = __builtin_fmaf(wp, v[j][i].x, acc[i].x);
+        acc[i].y = __builtin_fmaf(wp, v[j][i].y, acc[i].y);
+        acc[i].z = __builtin_fmaf(wp, v[j][i].z, acc[i].z);
+        acc[i].w = __builtin_fmaf(wp, v[j][i].w, acc[i].w);
+      }
+    }
+  }
+  const float inv = Wsum > 0.0f ? 1.0f / Wsum : 0.0f;
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -510,35 +688,94 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
     packed[2 * i] = (uint32_t)bf16_rn(v.x) | ((uint32_t)bf16_rn(v.y) << 16);
     packed[2 * i + 1] = (uint32_t)bf16_rn(v.z) | ((uint32_t)bf16_rn(v.w) << 16);
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(out + (int64_t)sh * kPaD + 16 * sub);
+  u32x4* dst = reinterpret_cast<u32x4*>(out + ((int64_t)s * num_heads + h) * kPaD + 16 * sub);
   dst[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
   dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
 }
 
+// Wave slots of the device for the partition kernels (three waves per SIMD,
+// four SIMDs per compute unit), cached per device.
+int partition_wave_slots() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 12;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cached[dev] = cus * 12;
+  }
+  return cached[dev];
+}
+
 }  // namespace
+
+// Units of the balanced split, or 0 for the fixed split: the balanced one
+// needs more than one partition of workspace per sequence, at most 64 * 64
+// sequences (the prefix of their block counts is one lane's range each),
+// and room in the workspace for num_units + num_seqs rows and the
+// per-sequence records with units of at most 32 blocks.  It aims at one
+// wave per wave slot.
+int64_t paged_attention_balanced_units(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t partition_size,
+                                       int wave_slots) {
+  const int64_t max_parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+  if (max_parts < 2 || num_seqs < 1 || num_seqs > kWave * kWave) return 0;
+  const int64_t cap_blocks = max_parts * partition_size / kPaWaveTokens;
+  const int64_t n_max = (int64_t)num_seqs * cap_blocks;
+  if (n_max >= INT32_MAX) return 0;
+  const int64_t u_min = (n_max + 31) / 32;
+  // rows num_units + num_seqs, then two int32 per sequence
+  const int64_t u_cap = (int64_t)num_seqs * (max_parts - 1) -
+                        (2 * (int64_t)num_seqs + num_heads - 1) / num_heads;
+  if (u_cap < u_min) return 0;
+  const int64_t groups = (num_kv_heads + kPaWaves - 1) / kPaWaves;
+  const int64_t active = num_kv_heads < kPaWaves ? num_kv_heads : kPaWaves;
+  int64_t u = (wave_slots + groups * active - 1) / (groups * active);
+  if (u < u_min) u = u_min;
+  if (u > u_cap) u = u_cap;
+  if (u * groups >= INT32_MAX) return 0;
+  return u;
+}
 
 int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t stream) {
   const int32_t P = a.partition_size;
   const int32_t max_parts = (a.max_context_len + P - 1) / P;
+  const int32_t token_cap = max_parts * P;
   const int64_t groups = (a.num_kv_heads + kPaWaves - 1) / kPaWaves;
-  const int64_t units = (int64_t)a.num_seqs * max_parts * groups;
-  if (units > 0) {
-    auto kernel = a.block_size == 16 ? paged_attention_partition_kernel<16>
-                                     : paged_attention_partition_kernel<0>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kPaThreads), 0, stream,
-                       (uint32_t)units, a.out, a.exp_sums, a.max_logits, a.tmp_out, a.query, a.key_cache,
-                       a.value_cache, a.block_tables, a.context_lens, a.num_seqs, a.num_heads,
-                       a.num_kv_heads, a.block_size, FastDiv::make((uint32_t)a.block_size),
-                       a.max_blocks_per_seq, max_parts, P, a.num_blocks, a.scale, a.k_scale,
-                       a.v_scale);
+  const int64_t bal = paged_attention_balanced_units(a.num_seqs, a.num_heads, a.num_kv_heads,
+                                                     a.max_context_len, P, partition_wave_slots());
+  const FastDiv bdiv = FastDiv::make((uint32_t)a.block_size);
+  if (bal > 0) {
+    auto kernel = a.block_size == 16 ? paged_attention_balanced_kernel<16>
+                                     : paged_attention_balanced_kernel<0>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(bal * groups)), dim3(kPaThreads), 0, stream,
+                       (uint32_t)bal, a.out, a.exp_sums, a.max_logits, a.tmp_out, a.query,
+                       a.key_cache, a.value_cache, a.block_tables, a.context_lens, a.num_seqs,
+                       a.num_heads, a.num_kv_heads, a.block_size, bdiv, a.max_blocks_per_seq,
+                       token_cap, a.num_blocks, a.scale, a.k_scale, a.v_scale);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return (int)e;
+  } else {
+    const int64_t units = (int64_t)a.num_seqs * max_parts * groups;
+    if (units > 0) {
+      auto kernel = a.block_size == 16 ? paged_attention_partition_kernel<16>
+                                       : paged_attention_partition_kernel<0>;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)units), dim3(kPaThreads), 0, stream,
+                         (uint32_t)units, a.out, a.exp_sums, a.max_logits, a.tmp_out, a.query,
+                         a.key_cache, a.value_cache, a.block_tables, a.context_lens, a.num_seqs,
+                         a.num_heads, a.num_kv_heads, a.block_size, bdiv, a.max_blocks_per_seq,
+                         max_parts, P, a.num_blocks, a.scale, a.k_scale, a.v_scale);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return (int)e;
+    }
   }
-  const int64_t rows = (int64_t)a.num_seqs * a.num_heads;
-  const int64_t rows_per_block = (int64_t)kPaWaves * kRdRowsPerWave;
-  hipLaunchKernelGGL(paged_attention_reduce_kernel, dim3((unsigned)((rows + rows_per_block - 1) / rows_per_block)),
+  const int64_t waves = (int64_t)a.num_seqs * ((a.num_heads + 7) / 8);
+  hipLaunchKernelGGL(paged_attention_reduce_kernel, dim3((unsigned)((waves + kPaWaves - 1) / kPaWaves)),
                      dim3(kPaThreads), 0, stream, a.out, a.exp_sums, a.max_logits, a.tmp_out,
-                     a.context_lens, a.num_seqs, a.num_heads, max_parts, P);
+                     a.context_lens, a.num_seqs, a.num_heads, max_parts, P, (uint32_t)bal,
+                     token_cap);
   return (int)hipGetLastError();
 }
 

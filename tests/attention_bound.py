@@ -12,22 +12,30 @@ W = sum_t w_t, o = sum_t w_t v_t / W:
    (4x the accumulation bound).
 2. Exponentials.  Logits are scaled by log2(e) (in binary32) and each
    weight is a product of hardware exp2 values: the token's own (against a
-   reference point that trails the running maximum by at most 2^8), up to
-   one rescale factor per 64-token block of its partition (at most 8), and
-   the partition's weight in the final combination.  Each has relative
-   error <= 2^-23 + 2^-24 |x| for an argument x of natural size; the |x|
-   along one product sum to at most 3 (R + 8 ln 2), with R the logit range
-   of the row.  Together with 1., the device weights are w_t (1 + g_t) with
-   |g_t| <= gamma = max_t expm1(2 delta_t) + 2^-18 (1 + R) (the factor 2 on
-   delta covers the shifted reference).
+   reference point that trails the running maximum by at most 2^8), one
+   rescale factor per later move of the reference point (a move raises it
+   by more than 8 in log2 units, so there are at most R log2(e) / 8 of
+   them, R the logit range of the row, however many blocks a partition
+   has), the partition's weight in the final combination, and one rescale
+   factor per later group of four partitions that raises the combination's
+   running maximum (at most 8 of them for 33 partitions).  Each has
+   relative error <= 2^-23 + 2^-24 |x| for an argument x of natural size;
+   the |x| along one product sum to at most 3 (R + 8 ln 2) + R.  So a
+   product of (10 + R/5) factors is within (10 + R/5) 2^-23 +
+   (4 R + 17) 2^-24 <= 2^-18 (1 + R).  Together with 1., the device weights are w_t (1 + g_t)
+   with |g_t| <= gamma = max_t expm1(2 delta_t) + 2^-18 (1 + R) (the factor
+   2 on delta covers the shifted reference).
    Perturbing the weights moves the result by at most
        gamma / (1 - gamma) * C,   C = sum_t w_t |v_t - o| / W.
-3. The P.V product and the sums.  Probabilities enter the bf16 MFMA as a
-   hi + lo pair (relative error <= 2^-17), accumulate in binary32 over at
-   most 256 tokens x 2 (<= 2^-15 of sum w|v|), and are normalised by the
-   partition's exp-sum; the exp-sums (<= 256 terms) and the partition
-   combination add <= 2^-15 relative to the denominator.  With alpha = beta =
-   2^-14 (2x margin):
+3. The P.V product and the sums.  A partition covers at most 2048 tokens.
+   Probabilities enter the bf16 MFMA as a hi + lo pair (relative error
+   <= 2^-17) and accumulate in binary32 over at most 2048 tokens x 2 terms,
+   each addition rounded (<= 2^12 * 2^-24 = 2^-12 of sum w|v|); they are
+   normalised by the partition's exp-sum.  The exp-sum takes at most 2048
+   terms in per-lane sums of 16 per block (<= 32 * 17 + 2 roundings), and
+   the normalisation and the combination of at most 33 partitions about 70
+   more: <= 2^-14.8 relative to the denominator.  With alpha = 2^-11 and
+   beta = 2^-13 (about 2x margin):
        E = gamma C / (1 - gamma) + (alpha A (1 + gamma) + beta (|o| + gamma C)) / (1 - beta),
        A = sum_t w_t |v_t| / W.
 4. The bf16 output rounds to nearest (8 significant bits): + 2^-8 (|o| + E).
@@ -91,7 +99,7 @@ def attention_bound(query_bits, key_cache, value_cache, block_tables, context_le
                 delta = 2.0 ** -15 * absdot + 2.0 ** -21 * np.abs(l)
                 R = l.max(1) - l.min(1)
                 gamma = (np.expm1(2 * delta).max(1) + 2.0 ** -18 * (1 + R))[:, None]
-                alpha = beta = 2.0 ** -14
+                alpha, beta = 2.0 ** -11, 2.0 ** -13
                 E = gamma * C / (1 - gamma) + (alpha * A * (1 + gamma) +
                                                beta * (np.abs(o) + gamma * C)) / (1 - beta)
                 bnd[kvh * G:(kvh + 1) * G] = E + 2.0 ** -8 * (np.abs(o) + E)

@@ -28,7 +28,7 @@ def bound_of(c):
                            c.num_kv_heads, c.scale, c.k_scale, c.v_scale)
 
 
-@pytest.mark.parametrize("P", [64, 512])
+@pytest.mark.parametrize("P", [64, 512, 2048])
 def test_bound_holds_for_a_binary32_model(P):
     c = case()
     ref, b = ref_of(c), bound_of(c)

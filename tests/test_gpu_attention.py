@@ -10,6 +10,7 @@ import torch
 import oracle
 import workloads
 from attention_bound import attention_bound
+from test_attention_split import balanced_units
 
 pytestmark = pytest.mark.gpu
 
@@ -123,6 +124,37 @@ def test_repeated_calls_share_a_workspace_on_a_side_stream():
         g2 = run(c2, 256, max_context_len=2000, stream=s, ws=ws)
     check(g1, *reference(c1))
     check(g2, *reference(c2))
+
+
+@pytest.mark.parametrize("P,balanced", [(2048, False), (512, True), (64, True)])
+def test_both_work_splits_on_a_mixed_batch(P, balanced):
+    """Contexts from one token to 4000 (whole-partition and ragged ends, a
+    sequence inside one unit and sequences across many), through the fixed
+    split (one partition per 2048 tokens) and the balanced one."""
+    lens = [1, 64, 65, 700, 2048, 1500, 4000, 3, 129, 2047, 999, 0, 64, 3333]
+    H, KVH = 32, 4
+    assert (balanced_units(len(lens), H, KVH, max(lens), P, 3072) > 0) == balanced
+    banner(f"paged attention work split P={P} balanced={balanced}")
+    c = workloads.paged_attention_case(50 + P, len(lens), H, KVH, lens=lens)
+    ref, b = reference(c)
+    worst = check(run(c, P), ref, b)
+    print(f"max err / bound = {worst:.3g}", flush=True)
+
+
+@pytest.mark.parametrize("S,balanced", [(4096, True), (4100, False)])
+def test_many_sequences(S, balanced):
+    """The most sequences the balanced split takes (their block counts fill
+    one lane's range each), and just past it (the fixed split)."""
+    lens = workloads.rng(60 + S).integers(0, 300, size=S).tolist()
+    lens[5] = 300
+    assert (balanced_units(S, 8, 1, 300, 64, 3072) > 0) == balanced
+    banner(f"paged attention {S} sequences, balanced={balanced}")
+    c = workloads.paged_attention_case(60 + S, S, 8, 1, lens=lens)
+    got = run(c, 64, max_context_len=300)
+    rows = sorted({5, *range(0, S, 97), S - 1})
+    ref, b = reference(c, rows)
+    worst = check(got[rows], ref, b)
+    print(f"rows sampled: max err / bound = {worst:.3g}", flush=True)
 
 
 def test_decode_batch_sampled():
