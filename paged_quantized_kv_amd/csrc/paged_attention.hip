@@ -27,8 +27,9 @@
 // head (the G = num_heads/num_kv_heads heads of the kv head are the 16
 // columns; columns >= G are zero).  fp8 keys and values become bf16 exactly
 // (4 significant bits fit in 8).  The wave walks its partition in blocks of
-// 64 tokens: per block each lane issues eight 16-byte key rows and eight
-// 16-byte value rows (16 KB per wave), and the next block's keys are
+// 64 tokens: per block each lane issues eight 16-byte key rows (whole-line
+// loads, rearranged for the MFMA by DPP row rotations) and eight 16-byte
+// value rows (16 KB per wave), and the next block's keys are
 // requested as soon as the logits are formed, its values as soon as the P.V
 // product has consumed the current ones.  A running softmax per head (the
 // maximum reduced over the four lane groups with the gfx950 lane-swap
@@ -159,6 +160,33 @@ __device__ __forceinline__ void split_bf16x8(const float (&p)[8], v8bf& hi, v8bf
   lo = __builtin_bit_cast(v8bf, u32x4{l[0], l[1], l[2], l[3]});
 }
 
+// Key operand of logits MFMA M from whole-line key loads.  kw[tt][h] holds,
+// in lane (c, g), the 16-byte key row of token c of tile tt at d/16 = g + 4h;
+// MFMA M needs in lane (col, grp) the row of token 4 M + col%4 of tile col/4
+// at the same d/16, i.e. lane (4 M + col%4, grp) of kw[col/4][h]: within each
+// 16-lane row, bank col/4 (lanes 4 (col/4) .. + 3) rotated by 4 (col/4 - M)
+// lanes.  One DPP row rotation per other tile, each writing its own bank.
+template <int kTile, int kM>
+__device__ __forceinline__ uint32_t bank_from_tile(uint32_t acc, uint32_t src) {
+  constexpr int n = (4 * (kTile - kM)) & 15;  // row_ror:n -- lane i takes lane (i - n) mod 16
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)acc, (int)src, 0x120 + n, 0xF, 1 << kTile,
+                                               false);
+}
+template <int kM, int kH>
+__device__ __forceinline__ uint32_t key_operand_dword(const u32x4 (&kw)[kPaTiles][2], int d) {
+  uint32_t x = kw[kM][kH][d];  // bank kM: no rotation
+  if constexpr (kM != 0) x = bank_from_tile<0, kM>(x, kw[0][kH][d]);
+  if constexpr (kM != 1) x = bank_from_tile<1, kM>(x, kw[1][kH][d]);
+  if constexpr (kM != 2) x = bank_from_tile<2, kM>(x, kw[2][kH][d]);
+  if constexpr (kM != 3) x = bank_from_tile<3, kM>(x, kw[3][kH][d]);
+  return x;
+}
+template <int kM, int kH>
+__device__ __forceinline__ u32x4 key_operand(const u32x4 (&kw)[kPaTiles][2]) {
+  return u32x4{key_operand_dword<kM, kH>(kw, 0), key_operand_dword<kM, kH>(kw, 1),
+               key_operand_dword<kM, kH>(kw, 2), key_operand_dword<kM, kH>(kw, 3)};
+}
+
 // One of four uniform values, chosen by a per-lane index in [0, 4): a select
 // chain on the values as scalars (readfirstlane makes them opaque, so the
 // selects cannot become an indexed access to the array, which would put the
@@ -228,23 +256,25 @@ __device__ __forceinline__ void attend_segment(
   for (int c = 0; c < 4; ++c)
     qv[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * (grp + 4 * (c >> 1)) + 8 * (c & 1));
 
-  // Loads of one 64-token block.  Keys: for logits MFMA m, lane (col, grp)
-  // holds the 16-byte key rows grp and grp + 4 of token 16 (col/4) + 4m +
-  // col%4.  Values: the 16 tokens of tile grp at d = 16n + col.  Tiles
-  // without a valid page read page 0 (in bounds) and are masked when used.
-  u32x4 kw[4][2];
+  // Loads of one 64-token block.  Keys: kw[tt][h] holds in lane (col, grp)
+  // the 16-byte key row of token col of tile tt at d/16 = grp + 4h (whole
+  // lines; key_operand rearranges them per MFMA).  Values: the 16 tokens of
+  // tile grp at d = 16n + col.  Tiles without a valid page read page 0 (in
+  // bounds) and are masked when used.
+  u32x4 kw[kPaTiles][2];
   u32x4 vw[8];
   auto issue_keys = [&](const int32_t (&pg)[kPaTiles], int32_t tb) {
-    const int32_t p = pick4(pg, col >> 2);
-    const uint32_t t0 = (uint32_t)(tb + (col >> 2) * 16);
-    const uint32_t off0 = t0 - bdiv.div(t0) * (uint32_t)block_size;
-    const uint8_t* kp = kbase + (int64_t)(p >= 0 ? p : 0) * kpage +
-                        ((int64_t)grp * block_size + off0 + (col & 3)) * 16;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int tt = 0; tt < kPaTiles; ++tt) {
+      const int32_t p = pg[tt];
+      const uint32_t t0 = (uint32_t)(tb + tt * 16);
+      const uint32_t off0 = t0 - bdiv.div(t0) * (uint32_t)block_size;
+      const uint8_t* kp = kbase + (int64_t)(p >= 0 ? p : 0) * kpage +
+                          ((int64_t)grp * block_size + off0 + col) * 16;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        kw[m][h] = *reinterpret_cast<const u32x4*>(kp + ((int64_t)4 * h * block_size + 4 * m) * 16);
+        kw[tt][h] = *reinterpret_cast<const u32x4*>(kp + (int64_t)4 * h * block_size * 16);
+    }
   };
   auto issue_values = [&](const int32_t (&pg)[kPaTiles], int32_t tb) {
     const int32_t p = pick4(pg, grp);
@@ -298,14 +328,19 @@ __device__ __forceinline__ void attend_segment(
     v4f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u32x4 w = kw[m][c >> 1];
-        const u32x2 half = (c & 1) ? u32x2{w.z, w.w} : u32x2{w.x, w.y};
-        acc[m] = mfma_bf16(fp8x8_to_bf16(half), bq[c], acc[m]);
-      }
+    auto tile_logits = [&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      const u32x4 w0 = key_operand<m, 0>(kw);
+      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w0.x, w0.y}), bq[0], acc[m]);
+      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w0.z, w0.w}), bq[1], acc[m]);
+      const u32x4 w1 = key_operand<m, 1>(kw);
+      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w1.x, w1.y}), bq[2], acc[m]);
+      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w1.z, w1.w}), bq[3], acc[m]);
+    };
+    tile_logits(std::integral_constant<int, 0>{});
+    tile_logits(std::integral_constant<int, 1>{});
+    tile_logits(std::integral_constant<int, 2>{});
+    tile_logits(std::integral_constant<int, 3>{});
     float lg[4][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
