@@ -347,12 +347,12 @@ __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_kernel(
 // codes and block scales, H*B*(D/2 + D/16) contiguous bytes -- into its LDS
 // slice with 16-byte loads that write LDS directly (global_load_lds_dwordx4:
 // lane i's 16 bytes land at the instruction's LDS base + 16 i, no registers
-// held), then produces the same units in the same order, reading each unit's
-// code dword and scale byte from LDS.  The 4- and 1-byte global loads of the
-// direct kernel become whole-line loads; bytes of the page past the run are
-// read but not used.
+// held), then produces the same units, reading each unit's code dword and
+// scale byte from LDS.  The 4- and 1-byte global loads of the direct kernel
+// become whole-line loads; bytes of the page past the run are read but not
+// used.
 constexpr int kFp4StageMax = 16384;  // bytes of one page side, at most
-constexpr int kFp4EmitUnroll = 4;    // units per lane in flight while emitting
+constexpr int kFp4EmitUnroll = 16;   // tokens per lane in flight while emitting
 
 template <int kD, bool kF16, int kChunks>  // kChunks: 16-byte loads per lane, at most
 __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_staged_kernel(
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_staged_kerne
     const int32_t* __restrict__ cu_seq_lens, int32_t num_reqs, int32_t max_blocks,
     int64_t num_tokens, int32_t num_heads, int32_t block_size, int64_t num_blocks,
     int64_t page_stride, int32_t layout, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, FastDiv upt_div, int32_t side_bytes) {
+    const float* __restrict__ v_scale, int32_t side_bytes) {
   extern __shared__ __align__(16) uint8_t stage_lds[];  // [kDqWaves][side_bytes]
   constexpr int S = kD / 16;       // blocks (scale bytes) per token head
   constexpr int hpt = kD / 8;      // half-blocks per token head
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_staged_kerne
   const int wave = threadIdx.x / kWave;
   uint8_t* stage = stage_lds + (int64_t)wave * side_bytes;
   const float ts_k = *k_scale, ts_v = *v_scale;
-  const int32_t upt = num_heads * hpt;  // half-blocks per token (upt_div divides by it)
+  const int32_t upt = num_heads * hpt;  // half-blocks per token
   const int32_t data_per_side = num_heads * block_size * data_dim;
   const int32_t chunks = side_bytes / 16;
   const int64_t units_total = (int64_t)num_reqs * max_blocks * 2;
@@ -399,54 +399,60 @@ __global__ __launch_bounds__(kDqThreads) void gather_kv_fp4_dequant_staged_kerne
     __builtin_amdgcn_s_waitcnt(0);  // every load of this wave has written LDS
     wave_sync();
 
-    // ---- units in output order, from LDS
+    // ---- units from LDS.  Lane slot r (= half-block hb of head h within a
+    // token row of upt half-blocks) is fixed for a pass over the run's
+    // tokens, so the code and scale offsets of token offset `off` are a base
+    // plus a per-token step: codes at cbase + off * cstep, scales at
+    // sbase + (off >> ssh) * sstep + (off & smask) (V scales are swizzled in
+    // groups of four tokens).  Each pass stores 64 consecutive units of a
+    // token row (1 KB) per instruction.
     const uint8_t* scales = stage + data_per_side;
     uint16_t* orow = (kv ? value_out : key_out) + run.row * (kv ? value_row_stride : key_row_stride);
     const int64_t out_stride = kv ? value_row_stride : key_row_stride;
     const float ts = kv ? ts_v : ts_k;
-    const int32_t units = (int32_t)run.rows * upt;
-    for (int32_t c0 = 0; c0 < units; c0 += kWave * kFp4EmitUnroll) {
-      uint32_t v[kFp4EmitUnroll], sb[kFp4EmitUnroll];
-#pragma unroll
-      for (int u = 0; u < kFp4EmitUnroll; ++u) {
-        const int32_t c = c0 + u * kWave + lane;
-        v[u] = 0u;
-        sb[u] = 0u;
-        if (c < units) {
-          const int32_t t = (int32_t)upt_div.div((uint32_t)c);
-          const int32_t r = c - t * upt;
-          const int32_t h = r / hpt;
-          const int32_t hb = r - h * hpt;  // half-block within the head
-          const int32_t g = hb >> 1;
-          const int32_t off = (int32_t)run.first + t;
-          const int32_t row = layout == PKV_LAYOUT_HND ? h * block_size + off : off * num_heads + h;
-          v[u] = *reinterpret_cast<const uint32_t*>(stage + row * data_dim + hb * 4);
-          int32_t so;
-          if (kv == 0) {
-            so = row * S + g;
-          } else {
-            // swizzled: (t', s') = ((off/4)*4 + g/(S/4), (g % (S/4))*4 + off%4)
-            const int32_t gq = g / (S / 4);
-            const int32_t gr = g - gq * (S / 4);
-            const int32_t srow = (off >> 2) * 4 + gq;
-            const int32_t col = gr * 4 + (off & 3);
-            so = (layout == PKV_LAYOUT_HND ? (h * block_size + srow) * S
-                                           : (srow * num_heads + h) * S) + col;
-          }
-          sb[u] = scales[so];
-        }
+    const int32_t rows = (int32_t)run.rows;
+    const bool hnd = layout == PKV_LAYOUT_HND;
+    for (int32_t r0 = 0; r0 < upt; r0 += kWave) {
+      const int32_t r = r0 + lane;
+      const bool live = r < upt;
+      const int32_t h = r / hpt;
+      const int32_t hb = r - h * hpt;
+      const int32_t g = hb >> 1;
+      const int32_t cbase = (hnd ? h * block_size : h) * data_dim + hb * 4;
+      const int32_t cstep = hnd ? data_dim : num_heads * data_dim;
+      int32_t sbase, sstep, ssh, smask;
+      if (kv == 0) {
+        sbase = (hnd ? h * block_size : h) * S + g;
+        sstep = hnd ? S : num_heads * S;
+        ssh = 0;
+        smask = 0;
+      } else {
+        // swizzled: token offset off, block g -> row (off/4)*4 + g/(S/4), column (g % (S/4))*4 + off%4
+        const int32_t gq = g / (S / 4);
+        const int32_t gr = g - gq * (S / 4);
+        sbase = (hnd ? (h * block_size + gq) * S : (gq * num_heads + h) * S) + gr * 4;
+        sstep = hnd ? 4 * S : 4 * num_heads * S;
+        ssh = 2;
+        smask = 3;
       }
+      uint16_t* obase = orow + (int64_t)r * 8;
+      for (int32_t t0 = 0; t0 < rows; t0 += kFp4EmitUnroll) {
+        uint32_t v[kFp4EmitUnroll], sb[kFp4EmitUnroll];
 #pragma unroll
-      for (int u = 0; u < kFp4EmitUnroll; ++u) {
-        const int32_t c = c0 + u * kWave + lane;
-        if (c >= units) continue;
-        const int32_t t = (int32_t)upt_div.div((uint32_t)c);
-        const float sfd = __builtin_amdgcn_cvt_f32_fp8((int)sb[u], 0);
-        const u32x4 o = {fp4_pair<0, kF16>(v[u], sfd, ts), fp4_pair<1, kF16>(v[u], sfd, ts),
-                         fp4_pair<2, kF16>(v[u], sfd, ts), fp4_pair<3, kF16>(v[u], sfd, ts)};
-        store_stream(reinterpret_cast<u32x4*>(orow + (int64_t)t * out_stride +
-                                              (int64_t)(c - t * upt) * 8),
-                     o);
+        for (int u = 0; u < kFp4EmitUnroll; ++u) {
+          const int32_t off = (int32_t)run.first + t0 + u;
+          const bool on = live && t0 + u < rows;
+          v[u] = on ? *reinterpret_cast<const uint32_t*>(stage + cbase + off * cstep) : 0u;
+          sb[u] = on ? scales[sbase + (off >> ssh) * sstep + (off & smask)] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < kFp4EmitUnroll; ++u) {
+          if (!live || t0 + u >= rows) continue;
+          const float sfd = __builtin_amdgcn_cvt_f32_fp8((int)sb[u], 0);
+          const u32x4 o = {fp4_pair<0, kF16>(v[u], sfd, ts), fp4_pair<1, kF16>(v[u], sfd, ts),
+                           fp4_pair<2, kF16>(v[u], sfd, ts), fp4_pair<3, kF16>(v[u], sfd, ts)};
+          store_stream(reinterpret_cast<u32x4*>(obase + (int64_t)(t0 + u) * out_stride), o);
+        }
       }
     }
   }
@@ -502,13 +508,12 @@ int launch_fp4_staged(const GatherFp4DequantArgs& a, int64_t units, int32_t side
   if (chunks <= 4) kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 4>;
   else if (chunks <= 8) kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 8>;
   else if (chunks <= 12) kernel = gather_kv_fp4_dequant_staged_kernel<kD, kF16, 12>;
-  const uint32_t upt = (uint32_t)(a.num_heads * (kD / 8));
   hipLaunchKernelGGL(kernel, dim3((unsigned)dq_blocks(units)), dim3(kDqThreads),
                      (size_t)kDqWaves * side_bytes, stream, a.key_cache, a.value_cache, a.key_out,
                      a.key_row_stride, a.value_out, a.value_row_stride, a.block_table,
                      a.cu_seq_lens, a.num_reqs, a.max_blocks_per_req, a.num_tokens, a.num_heads,
                      a.block_size, a.num_blocks, a.page_stride, a.layout, a.k_scale, a.v_scale,
-                     FastDiv::make(upt), side_bytes);
+                     side_bytes);
   return (int)hipGetLastError();
 }
 
