@@ -16,15 +16,19 @@ W = sum_t w_t, o = sum_t w_t v_t / W:
    rescale factor per later move of the reference point (a move raises it
    by more than 8 in log2 units, so there are at most R log2(e) / 8 of
    them, R the logit range of the row, however many blocks a partition
-   has), the partition's weight in the final combination, and one rescale
-   factor per later group of four partitions that raises the combination's
-   running maximum (at most 8 of them for 33 partitions).  Each has
-   relative error <= 2^-23 + 2^-24 |x| for an argument x of natural size;
-   the |x| along one product sum to at most 3 (R + 8 ln 2) + R.  So a
-   product of (10 + R/5) factors is within (10 + R/5) 2^-23 +
-   (4 R + 17) 2^-24 <= 2^-18 (1 + R).  Together with 1., the device weights are w_t (1 + g_t)
-   with |g_t| <= gamma = max_t expm1(2 delta_t) + 2^-18 (1 + R) (the factor
-   2 on delta covers the shifted reference).
+   has), the partial's weight in the final combination, and one rescale
+   factor per later group of four partials that raises the combination's
+   running maximum (at most ceil(n_p / 4) for n_p partials).  A row has at
+   most n_p = ceil(L / 64) + 1 partials under either work split (a segment
+   is at least one 64-token block; the balanced split adds at most one
+   segment per sequence).  Each factor has relative error <= 2^-23 +
+   2^-24 |x| for an argument x of natural size; the |x| along one product
+   sum to at most 3 (R + 8 ln 2) + R.  So the product of (2 + R/5 +
+   ceil(n_p/4)) factors is within
+       rho = (2 + R/5 + ceil(n_p/4)) 2^-23 + (4 R + 17) 2^-24.
+   Together with 1., the device weights are w_t (1 + g_t) with
+   |g_t| <= gamma = max_t expm1(2 delta_t) + 2 rho (the factor 2 on delta
+   covers the shifted reference, the one on rho is margin).
    Perturbing the weights moves the result by at most
        gamma / (1 - gamma) * C,   C = sum_t w_t |v_t - o| / W.
 3. The P.V product and the sums.  A partition covers at most 2048 tokens.
@@ -32,10 +36,11 @@ W = sum_t w_t, o = sum_t w_t v_t / W:
    <= 2^-17) and accumulate in binary32 over at most 2048 tokens x 2 terms,
    each addition rounded (<= 2^12 * 2^-24 = 2^-12 of sum w|v|); they are
    normalised by the partition's exp-sum.  The exp-sum takes at most 2048
-   terms in per-lane sums of 16 per block (<= 32 * 17 + 2 roundings), and
-   the normalisation and the combination of at most 33 partitions about 70
-   more: <= 2^-14.8 relative to the denominator.  With alpha = 2^-11 and
-   beta = 2^-13 (about 2x margin):
+   terms in per-lane sums of 16 per block (<= 32 * 17 + 2 roundings), the
+   normalisation 3 more and the combination of n_p partials at most 3 n_p
+   + 2 (the weighted sums, their rescalings and the final reciprocal): at
+   most (551 + 3 n_p) 2^-24 relative to the denominator.  With alpha =
+   2^-11 (2x margin) and beta = (551 + 3 n_p) 2^-23 (2x margin):
        E = gamma C / (1 - gamma) + (alpha A (1 + gamma) + beta (|o| + gamma C)) / (1 - beta),
        A = sum_t w_t |v_t| / W.
 4. The bf16 output rounds to nearest (8 significant bits): + 2^-8 (|o| + E).
@@ -85,6 +90,7 @@ def attention_bound(query_bits, key_cache, value_cache, block_tables, context_le
             kc = e4m3_decode(key_cache[pages, :, :, offs, :]).reshape(pages.size, num_kv_heads, D)
             vv = e4m3_decode(value_cache[pages, :, :, offs]) * v_scale      # [n, KVH, D]
             sk = float(scale) * float(k_scale)
+            n_p = -(-int(context_lens[s]) // 64) + 1
             for kvh in range(num_kv_heads):
                 qh = q_all[s, kvh * G:(kvh + 1) * G]                         # [G, D]
                 l = sk * (qh @ kc[:, kvh].T)                                 # [G, n]
@@ -98,8 +104,9 @@ def attention_bound(query_bits, key_cache, value_cache, block_tables, context_le
                 C = np.einsum("gt,gtd->gd", w, np.abs(Vh[None, :, :] - o[:, None, :])) / W
                 delta = 2.0 ** -15 * absdot + 2.0 ** -21 * np.abs(l)
                 R = l.max(1) - l.min(1)
-                gamma = (np.expm1(2 * delta).max(1) + 2.0 ** -18 * (1 + R))[:, None]
-                alpha, beta = 2.0 ** -11, 2.0 ** -13
+                rho = (2 + R / 5 + -(-n_p // 4)) * 2.0 ** -23 + (4 * R + 17) * 2.0 ** -24
+                gamma = (np.expm1(2 * delta).max(1) + 2 * rho)[:, None]
+                alpha, beta = 2.0 ** -11, (551 + 3 * n_p) * 2.0 ** -23
                 E = gamma * C / (1 - gamma) + (alpha * A * (1 + gamma) +
                                                beta * (np.abs(o) + gamma * C)) / (1 - beta)
                 bnd[kvh * G:(kvh + 1) * G] = E + 2.0 ** -8 * (np.abs(o) + E)
