@@ -126,16 +126,18 @@ def test_repeated_calls_share_a_workspace_on_a_side_stream():
     check(g2, *reference(c2))
 
 
-@pytest.mark.parametrize("P,balanced", [(2048, False), (512, True), (64, True)])
-def test_both_work_splits_on_a_mixed_batch(P, balanced):
+@pytest.mark.parametrize("P,B,balanced", [(2048, 16, False), (2048, 32, False), (512, 16, True),
+                                          (64, 16, True), (256, 32, True)])
+def test_both_work_splits_on_a_mixed_batch(P, B, balanced):
     """Contexts from one token to 4000 (whole-partition and ragged ends, a
     sequence inside one unit and sequences across many), through the fixed
-    split (one partition per 2048 tokens) and the balanced one."""
+    split (one partition per 2048 tokens) and the balanced one, with the
+    16-token page build and the generic one."""
     lens = [1, 64, 65, 700, 2048, 1500, 4000, 3, 129, 2047, 999, 0, 64, 3333]
     H, KVH = 32, 4
     assert (balanced_units(len(lens), H, KVH, max(lens), P, 3072) > 0) == balanced
-    banner(f"paged attention work split P={P} balanced={balanced}")
-    c = workloads.paged_attention_case(50 + P, len(lens), H, KVH, lens=lens)
+    banner(f"paged attention work split P={P} B={B} balanced={balanced}")
+    c = workloads.paged_attention_case(50 + P + B, len(lens), H, KVH, block_size=B, lens=lens)
     ref, b = reference(c)
     worst = check(run(c, P), ref, b)
     print(f"max err / bound = {worst:.3g}", flush=True)
