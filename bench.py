@@ -38,8 +38,9 @@ launches; the per-kernel durations come from the K steps that follow, with
 HIP events recorded on the launch stream around each launch (timing-only
 events, without the cache write-back a default event performs), and
 `ms_per_step_with_events` is those steps' wall clock; `roofline` describes
-the kernel with the longest average duration; `cpu_baseline` times the CPU
-oracle on the same batch (one thread).
+the kernel with the longest average duration; `d2d_copy_same_bytes` times a
+device-to-device copy moving the step's bytes (the practical ceiling);
+`cpu_baseline` times the CPU oracle on the same batch (one thread).
 """
 from __future__ import annotations
 
@@ -243,6 +244,31 @@ def time_reader(args, pkv, torch, timing, stream, sets, w, f, bt, cu, c4, k4s, v
     return ms
 
 
+def time_d2d_copy(torch, timing, stream, nbytes, reps=20):
+    """A device-to-device copy (torch's copy_, the runtime's copy kernel)
+    moving nbytes in all (half read, half written): the practical ceiling
+    the step's kernels are set against."""
+    half = (nbytes // 2 + 255) // 256 * 256
+    src = torch.empty(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = timing.create(), timing.create()
+    timing.record(e0, stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    timing.record(e1, stream)
+    torch.cuda.synchronize()
+    ms = timing.elapsed_ms(e0, e1) / reps
+    timing.destroy_all()
+    del src, dst
+    gbps = 2 * half / (ms * 1e-3) / 1e9
+    return {"bytes": 2 * half, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "what": "torch copy_ of half the step's algorithmic bytes (read + write = the step's bytes)"}
+
+
 def decode_attention_bytes(c):
     """Bytes decode attention must move: the K and V codes of every token of
     every sequence (each read once), the bf16 queries and outputs, and the
@@ -429,6 +455,7 @@ def main():
 
     alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
     step_bytes = sum(alg.values())
+    copy_ceiling = time_d2d_copy(torch, timing, stream, step_bytes)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     kernels = {}
     for n in names:
@@ -470,6 +497,7 @@ def main():
         "ms_per_step_with_events": round(wall_events * 1e3 / args.steps, 4),
         "kernels": kernels,
         "roofline": roofline,
+        "d2d_copy_same_bytes": copy_ceiling,
         "input_gen_s": round(t_gen, 1),
     }
     if reader is not None:
