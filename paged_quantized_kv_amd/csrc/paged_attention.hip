@@ -51,6 +51,7 @@
 //   out = sum_p l_p e^(m_p - M) o_p / sum_p l_p e^(m_p - M)
 // and rounds to bf16.  A sequence without a valid token gets a zero row;
 // tokens whose page id is outside [0, num_blocks) are left out.
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -729,19 +730,22 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
 }
 
 // Wave slots of the device for the partition kernels (three waves per SIMD,
-// four SIMDs per compute unit), cached per device.
+// four SIMDs per compute unit), cached per device (threads that race on the
+// first call store the same value).
 int partition_wave_slots() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * 12;
-  if (cached[dev] == 0) {
+  int slots = cached[dev].load(std::memory_order_relaxed);
+  if (slots == 0) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
       cus = 256;
-    cached[dev] = cus * 12;
+    slots = cus * 12;
+    cached[dev].store(slots, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return slots;
 }
 
 }  // namespace
