@@ -143,6 +143,25 @@ def test_both_work_splits_on_a_mixed_batch(P, B, balanced):
     print(f"max err / bound = {worst:.3g}", flush=True)
 
 
+@pytest.mark.parametrize("P,balanced", [(256, True), (1024, False)])
+def test_tokens_past_the_workspace_are_not_read(P, balanced):
+    """Only tokens below ceil(max_context_len / P) * P are read, under either
+    split: a context longer than that attends its first tokens only (the
+    caller broke the max_context_len contract; nothing past it is touched)."""
+    lens = [3000, 100, 700]
+    maxc = 1000
+    cap = -(-maxc // P) * P
+    assert (balanced_units(len(lens), 16, 2, maxc, P, 3072) > 0) == balanced
+    banner(f"paged attention contexts past max_context_len, P={P}")
+    c = workloads.paged_attention_case(80 + P, len(lens), 16, 2, lens=lens)
+    got = run(c, P, max_context_len=maxc)
+    capped = workloads.PagedAttentionCase(c.query, c.key_cache, c.value_cache, c.block_tables,
+                                          np.minimum(c.context_lens, cap).astype(np.int32),
+                                          c.num_kv_heads, c.scale, c.k_scale, c.v_scale)
+    ref, b = reference(capped)
+    check(got, ref, b)
+
+
 @pytest.mark.parametrize("S,balanced", [(4096, True), (4100, False)])
 def test_many_sequences(S, balanced):
     """The most sequences the balanced split takes (their block counts fill
