@@ -40,6 +40,8 @@ events, without the cache write-back a default event performs), and
 `ms_per_step_with_events` is those steps' wall clock; `roofline` describes
 the kernel with the longest average duration; `d2d_copy_same_bytes` times a
 device-to-device copy moving the step's bytes (the practical ceiling);
+`store_kv_fp4_alone` times the NVFP4 store back to back with the
+workload's slots and with the same tokens stored to pages in order;
 `cpu_baseline` times the CPU oracle on the same batch (one thread).
 """
 from __future__ import annotations
@@ -456,6 +458,32 @@ def main():
     alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
     step_bytes = sum(alg.values())
     copy_ceiling = time_d2d_copy(torch, timing, stream, step_bytes)
+
+    # The NVFP4 store alone, back to back, with the workload's slots and with
+    # the same tokens' slots in page order (same bytes, pages written in
+    # order rather than in the workload's shuffled order).
+    def store_alone(slots):
+        ev = [timing.create(), timing.create()]
+        for _ in range(5):
+            pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slots, k4s, v4s,
+                                 block_size=f.block_size, layout=f.layout)
+        torch.cuda.synchronize()
+        timing.record(ev[0], stream)
+        for _ in range(20):
+            pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slots, k4s, v4s,
+                                 block_size=f.block_size, layout=f.layout)
+        timing.record(ev[1], stream)
+        torch.cuda.synchronize()
+        ms = timing.elapsed_ms(ev[0], ev[1]) / 20
+        timing.destroy_all()
+        gbps = alg["store_kv_fp4"] / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
+                "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    slot_in_order = torch.arange(T, dtype=torch.int64, device=dev)
+    store_alone_runs = {"workload_slots": store_alone(slot4),
+                        "pages_in_order": store_alone(slot_in_order),
+                        "what": "store_kv_fp4 alone, 20 back-to-back launches: the workload's "
+                                "slots, and slots 0..T-1 (the same tokens into pages in order)"}
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     kernels = {}
     for n in names:
@@ -498,6 +526,7 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
         "d2d_copy_same_bytes": copy_ceiling,
+        "store_kv_fp4_alone": store_alone_runs,
         "input_gen_s": round(t_gen, 1),
     }
     if reader is not None:
