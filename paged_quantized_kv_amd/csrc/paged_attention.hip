@@ -756,9 +756,9 @@ int partition_wave_slots() {
 // and room in the workspace for num_units + num_seqs rows and the
 // per-sequence records with units of at most 32 blocks.  It aims at one
 // wave per wave slot.
-int64_t paged_attention_balanced_units(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                       int32_t max_context_len, int32_t partition_size,
-                                       int wave_slots) {
+static int64_t paged_attention_balanced_units(int32_t num_seqs, int32_t num_heads,
+                                              int32_t num_kv_heads, int32_t max_context_len,
+                                              int32_t partition_size, int wave_slots) {
   const int64_t max_parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
   if (max_parts < 2 || num_seqs < 1 || num_seqs > kWave * kWave) return 0;
   const int64_t cap_blocks = max_parts * partition_size / kPaWaveTokens;
