@@ -74,6 +74,10 @@
 
 #include <stdint.h>
 
+/* Every entry point is exported; the library is built with hidden
+ * visibility otherwise, so nothing else of it is. */
+#define PKV_API __attribute__((visibility("default")))
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -95,10 +99,10 @@ extern "C" {
 
 /* ABI version of this header; bumped when a signature changes. */
 #define PKV_ABI_VERSION 5
-int pkv_abi_version(void);
+PKV_API int pkv_abi_version(void);
 
 /* Message for the last non-zero status on this thread ("" if none). */
-const char *pkv_last_error(void);
+PKV_API const char *pkv_last_error(void);
 
 /*
  * Gather (vLLM PR "Add gather_indexer_k_quant_cache kernel").
@@ -126,12 +130,12 @@ const char *pkv_last_error(void);
  * Errors: PKV_EINVAL for negative sizes or missing pointers, PKV_EALIGN,
  * PKV_EUNSUPPORTED when head_dim % 16 != 0 or the stride is too small.
  */
-int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_scale,
-                             const int32_t *block_table, const int32_t *cu_seq_lens,
-                             int32_t num_reqs, int32_t max_blocks_per_req,
-                             int64_t num_tokens, int64_t num_blocks,
-                             int64_t cache_block_stride, int32_t block_size,
-                             int32_t head_dim, void *stream);
+PKV_API int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_scale,
+                                     const int32_t *block_table, const int32_t *cu_seq_lens,
+                                     int32_t num_reqs, int32_t max_blocks_per_req,
+                                     int64_t num_tokens, int64_t num_blocks,
+                                     int64_t cache_block_stride, int32_t block_size,
+                                     int32_t head_dim, void *stream);
 
 /*
  * fp8 per-token store into the indexer K cache (the producer of the pages
@@ -154,11 +158,11 @@ int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_scale,
  *   kv_cache      written; 16-byte aligned; stride as for the gather.
  *   head_dim      multiple of 16, at most 1024.
  */
-int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride, int32_t k_dtype,
-                            const int64_t *slot_mapping, int64_t num_tokens,
-                            void *kv_cache, int64_t num_blocks,
-                            int64_t cache_block_stride, int32_t block_size,
-                            int32_t head_dim, void *stream);
+PKV_API int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride, int32_t k_dtype,
+                                    const int64_t *slot_mapping, int64_t num_tokens,
+                                    void *kv_cache, int64_t num_blocks,
+                                    int64_t cache_block_stride, int32_t block_size,
+                                    int32_t head_dim, void *stream);
 
 /*
  * NVFP4 K/V store (vLLM nvfp4_kv_cache_kernels.cu).
@@ -192,13 +196,13 @@ int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride, int32_t k_dtype
  *   head_size       multiple of 64 (so each 4x4 swizzle tile is complete);
  *   block_size      multiple of 4.
  */
-int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
-                     int64_t value_row_stride, int32_t src_dtype, void *key_cache,
-                     void *value_cache,
-                     const int64_t *slot_mapping, int64_t num_tokens,
-                     int32_t num_heads, int32_t head_size, int32_t block_size,
-                     int64_t num_blocks, int64_t page_stride, int32_t layout,
-                     const float *k_scale, const float *v_scale, void *stream);
+PKV_API int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
+                             int64_t value_row_stride, int32_t src_dtype, void *key_cache,
+                             void *value_cache,
+                             const int64_t *slot_mapping, int64_t num_tokens,
+                             int32_t num_heads, int32_t head_size, int32_t block_size,
+                             int64_t num_blocks, int64_t page_stride, int32_t layout,
+                             const float *k_scale, const float *v_scale, void *stream);
 
 /*
  * Dequantising gather of the indexer K cache (the gather of vLLM PR "Add
@@ -225,12 +229,12 @@ int pkv_store_kv_fp4(const void *key, int64_t key_row_stride, const void *value,
  * Errors: as for the gather, plus PKV_EINVAL for a bad out_dtype or row
  * stride and PKV_EALIGN for a row stride that is not a multiple of 8.
  */
-int pkv_gather_indexer_k_dequant(const void *kv_cache, void *out, int64_t out_row_stride,
-                                 int32_t out_dtype, const int32_t *block_table,
-                                 const int32_t *cu_seq_lens, int32_t num_reqs,
-                                 int32_t max_blocks_per_req, int64_t num_tokens,
-                                 int64_t num_blocks, int64_t cache_block_stride,
-                                 int32_t block_size, int32_t head_dim, void *stream);
+PKV_API int pkv_gather_indexer_k_dequant(const void *kv_cache, void *out, int64_t out_row_stride,
+                                         int32_t out_dtype, const int32_t *block_table,
+                                         const int32_t *cu_seq_lens, int32_t num_reqs,
+                                         int32_t max_blocks_per_req, int64_t num_tokens,
+                                         int64_t num_blocks, int64_t cache_block_stride,
+                                         int32_t block_size, int32_t head_dim, void *stream);
 
 /*
  * NVFP4 K/V pages read back (the inverse of pkv_store_kv_fp4 up to its
@@ -263,15 +267,15 @@ int pkv_gather_indexer_k_dequant(const void *kv_cache, void *out, int64_t out_ro
  * NaN scale bytes (0x7F / 0xFF) are never written by the store; reading them
  * gives NaN (bits unspecified).
  */
-int pkv_gather_kv_fp4_dequant(const void *key_cache, const void *value_cache, void *key_out,
-                              int64_t key_row_stride, void *value_out,
-                              int64_t value_row_stride, int32_t out_dtype,
-                              const int32_t *block_table, const int32_t *cu_seq_lens,
-                              int32_t num_reqs, int32_t max_blocks_per_req,
-                              int64_t num_tokens, int32_t num_heads, int32_t head_size,
-                              int32_t block_size, int64_t num_blocks, int64_t page_stride,
-                              int32_t layout, const float *k_scale, const float *v_scale,
-                              void *stream);
+PKV_API int pkv_gather_kv_fp4_dequant(const void *key_cache, const void *value_cache, void *key_out,
+                                      int64_t key_row_stride, void *value_out,
+                                      int64_t value_row_stride, int32_t out_dtype,
+                                      const int32_t *block_table, const int32_t *cu_seq_lens,
+                                      int32_t num_reqs, int32_t max_blocks_per_req,
+                                      int64_t num_tokens, int32_t num_heads, int32_t head_size,
+                                      int32_t block_size, int64_t num_blocks, int64_t page_stride,
+                                      int32_t layout, const float *k_scale, const float *v_scale,
+                                      void *stream);
 
 /*
  * Indexer logits on the gathered keys (vLLM PR "[Deepseek-V3.2][Kernel]
@@ -305,11 +309,11 @@ int pkv_gather_kv_fp4_dequant(const void *key_cache, const void *value_cache, vo
  * PKV_EUNSUPPORTED without launching: a GPU run of its kernel on causal
  * per-request ranges did not finish, and the cause is not found yet.
  */
-int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void *k,
-                       const float *k_scale, const float *weights, const int32_t *ks,
-                       const int32_t *ke, float *logits, int64_t row_stride, int64_t row_cols,
-                       int32_t num_q, int32_t num_heads, int64_t num_k, int32_t head_dim,
-                       void *stream);
+PKV_API int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void *k,
+                               const float *k_scale, const float *weights, const int32_t *ks,
+                               const int32_t *ke, float *logits, int64_t row_stride, int64_t row_cols,
+                               int32_t num_q, int32_t num_heads, int64_t num_k, int32_t head_dim,
+                               void *stream);
 
 /*
  * Paged decode attention over fp8 pages (vLLM PR "[ROCm] Faster Custom Paged
@@ -366,14 +370,14 @@ int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void *k,
  * The workspace is the caller's: the library allocates nothing.  Calls that
  * share a workspace must be ordered on one stream.
  */
-int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_logits, float *tmp_out,
-                               const void *query, const void *key_cache,
-                               const void *value_cache, const int32_t *block_tables,
-                               const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
-                               int32_t num_kv_heads, int32_t head_size, int32_t block_size,
-                               int32_t max_blocks_per_seq, int32_t max_context_len,
-                               int64_t num_blocks, float scale, float k_scale, float v_scale,
-                               int32_t partition_size, void *stream);
+PKV_API int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_logits, float *tmp_out,
+                                       const void *query, const void *key_cache,
+                                       const void *value_cache, const int32_t *block_tables,
+                                       const int32_t *context_lens, int32_t num_seqs, int32_t num_heads,
+                                       int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                                       int32_t max_blocks_per_seq, int32_t max_context_len,
+                                       int64_t num_blocks, float scale, float k_scale, float v_scale,
+                                       int32_t partition_size, void *stream);
 
 
 /*
@@ -385,8 +389,8 @@ int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_logits, fl
  *                         every non-NaN y[i].
  * y: binary32 [n], 16-byte aligned; out: bytes [n]; n a multiple of 16.
  */
-int pkv_diag_encode_e4m3(const float *y, uint8_t *out, int64_t n, void *stream);
-int pkv_diag_encode_e2m1(const float *y, uint8_t *out, int64_t n, void *stream);
+PKV_API int pkv_diag_encode_e4m3(const float *y, uint8_t *out, int64_t n, void *stream);
+PKV_API int pkv_diag_encode_e2m1(const float *y, uint8_t *out, int64_t n, void *stream);
 
 /*
  * Diagnostic: the output rounding of the dequantising gathers,
@@ -394,7 +398,7 @@ int pkv_diag_encode_e2m1(const float *y, uint8_t *out, int64_t n, void *stream);
  * x: binary32 [n], 16-byte aligned; out: 16-bit [n], 16-byte aligned; n a
  * multiple of 16.  NaN inputs give NaN (bits unspecified).
  */
-int pkv_diag_narrow(const float *x, uint16_t *out, int64_t n, int32_t out_dtype, void *stream);
+PKV_API int pkv_diag_narrow(const float *x, uint16_t *out, int64_t n, int32_t out_dtype, void *stream);
 
 #ifdef __cplusplus
 }

@@ -37,6 +37,7 @@ CXXFLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
+    "-fvisibility=hidden",  # only the PKV_API entry points are exported
     # IEEE binary32 step by step: no a*b+c contraction except the explicit
     # fma calls; divisions stay correctly rounded; subnormals are kept.
     "-ffp-contract=off",

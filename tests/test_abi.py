@@ -19,7 +19,8 @@ A = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(pkv_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:PKV_API\s+)?(?:int|const char \*)\s*(pkv_\w+)\s*\(",
+                                 text, re.M)))
 
 
 def test_header_declares_the_boundary():
@@ -40,6 +41,11 @@ def test_library_exports_every_declared_symbol():
         assert s in exported, s
         assert getattr(lib, s) is not None
     assert pkv.abi_version() == 5
+    # nothing else of the library is exported (the compiler's own
+    # per-translation-unit ids aside)
+    others = [name for name in re.findall(r"^\S*\s*\S+ (\S+)$", out, re.M)
+              if not name.startswith(("pkv_", "__hip_cuid_"))]
+    assert others == [], others
 
 
 def lib():
