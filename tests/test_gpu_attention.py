@@ -162,6 +162,19 @@ def test_tokens_past_the_workspace_are_not_read(P, balanced):
     check(got, ref, b)
 
 
+def test_one_long_context_across_many_units():
+    """A 16K-token context beside a short one: the balanced split spreads the
+    long sequence over about 86 units, and the reduce combines that many
+    partials per head, four at a time."""
+    lens = [16384, 300]
+    assert balanced_units(2, 64, 8, max(lens), 256, 3072) > 100
+    banner("paged attention one 16K-token context")
+    c = workloads.paged_attention_case(91, len(lens), 64, 8, lens=lens)
+    ref, b = reference(c)
+    worst = check(run(c, 256), ref, b)
+    print(f"max err / bound = {worst:.3g}", flush=True)
+
+
 @pytest.mark.parametrize("S,balanced", [(4096, True), (4100, False)])
 def test_many_sequences(S, balanced):
     """The most sequences the balanced split takes (their block counts fill
