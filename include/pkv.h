@@ -379,6 +379,16 @@ PKV_API int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_lo
                                        int64_t num_blocks, float scale, float k_scale, float v_scale,
                                        int32_t partition_size, void *stream);
 
+/* Host-only query (no GPU work): the number of work units the balanced split
+ * of pkv_paged_attention_decode uses for these sizes when the device holds
+ * wave_slots partition-kernel waves at once (a compute unit holds 12), or 0
+ * when the call takes the fixed split of partitions of partition_size
+ * tokens.  Arguments as for pkv_paged_attention_decode; returns 0 for sizes
+ * that call would reject. */
+PKV_API int64_t pkv_attention_balanced_units(int32_t num_seqs, int32_t num_heads,
+                                             int32_t num_kv_heads, int32_t max_context_len,
+                                             int32_t partition_size, int32_t wave_slots);
+
 
 /*
  * Diagnostics: the device codecs the store kernels use, exposed so that a

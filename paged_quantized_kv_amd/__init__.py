@@ -19,6 +19,7 @@ import torch
 __all__ = [
     "pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
     "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant", "pkv_fp8_mqa_logits",
+    "pkv_paged_attention_decode", "paged_attention_workspace", "pkv_attention_balanced_units",
     "pkv_diag_narrow",
     "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "PkvError", "LAYOUT_HND", "LAYOUT_NHD",
     "library_path", "abi_version",
@@ -84,6 +85,8 @@ def _load():
     f32 = ctypes.c_float
     lib.pkv_paged_attention_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                                i32, i32, i64, f32, f32, f32, i32, P]
+    lib.pkv_attention_balanced_units.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.pkv_attention_balanced_units.restype = i64
     for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
                  "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
                  "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "pkv_diag_narrow",
@@ -500,3 +503,13 @@ def pkv_paged_attention_decode(out, exp_sums, max_logits, tmp_out, query, key_ca
         context_lens.data_ptr(), num_seqs, num_heads, num_kv_heads, head_size, block_size,
         block_tables.shape[1], max_context_len, num_blocks, scale, k_scale, v_scale,
         partition_size, _stream(stream)))
+
+
+def pkv_attention_balanced_units(num_seqs: int, num_heads: int, num_kv_heads: int,
+                                 max_context_len: int, partition_size: int,
+                                 wave_slots: int) -> int:
+    """Work units of pkv_paged_attention_decode's balanced split for these
+    sizes on a device holding wave_slots partition-kernel waves at once (12
+    per compute unit), or 0 for the fixed split.  Host only; no GPU work."""
+    return int(_lib.pkv_attention_balanced_units(num_seqs, num_heads, num_kv_heads,
+                                                 max_context_len, partition_size, wave_slots))

@@ -403,4 +403,15 @@ int pkv_diag_narrow(const float* x, uint16_t* out, int64_t n, int32_t out_dtype,
   return launched(pkv::launch_diag_narrow(x, out, n, out_dtype, static_cast<hipStream_t>(stream)), op);
 }
 
+int64_t pkv_attention_balanced_units(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                     int32_t max_context_len, int32_t partition_size,
+                                     int32_t wave_slots) {
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      max_context_len < 0 || max_context_len > (1 << 30) || partition_size < 64 ||
+      partition_size > 2048 || (partition_size & (partition_size - 1)) != 0 || wave_slots <= 0)
+    return 0;
+  return pkv::attention_balanced_units(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                       partition_size, wave_slots);
+}
+
 }  // extern "C"

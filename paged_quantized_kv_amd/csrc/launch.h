@@ -152,6 +152,10 @@ int launch_fp8_mqa_logits(const MqaLogitsArgs& a, hipStream_t stream);
 int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stream);
 int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream);
 int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t stream);
+// Units of the decode attention's balanced split for these sizes (0: fixed split).
+int64_t attention_balanced_units(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t partition_size,
+                                 int32_t wave_slots);
 int launch_store_indexer_k_fp8(const StoreFp8Args& a, hipStream_t stream);
 int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream);
 int launch_diag_e4m3(const float* y, uint8_t* out, int64_t n, hipStream_t stream);

@@ -778,6 +778,13 @@ static int64_t paged_attention_balanced_units(int32_t num_seqs, int32_t num_head
   return u;
 }
 
+int64_t attention_balanced_units(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t max_context_len, int32_t partition_size,
+                                 int32_t wave_slots) {
+  return paged_attention_balanced_units(num_seqs, num_heads, num_kv_heads, max_context_len,
+                                        partition_size, wave_slots);
+}
+
 int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t stream) {
   const int32_t P = a.partition_size;
   const int32_t max_parts = (a.max_context_len + P - 1) / P;

@@ -19,7 +19,7 @@ A = 1 << 20  # a 16-byte aligned fake device address; never dereferenced
 
 def declared_symbols():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:PKV_API\s+)?(?:int|const char \*)\s*(pkv_\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:PKV_API\s+)?(?:int64_t|int|const char \*)\s*(pkv_\w+)\s*\(",
                                  text, re.M)))
 
 

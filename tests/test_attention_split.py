@@ -204,3 +204,23 @@ def test_units_fit_the_workspace_and_the_table_slice():
                 max_parts = -(-maxc // P)
                 assert (U + S) * 64 + 2 * S <= S * max_parts * 64
                 assert math.ceil(S * (max_parts * P // 64) / U) <= 32
+
+
+def test_library_sizes_the_split_like_the_model():
+    """The library's host-side choice (pkv_attention_balanced_units, no GPU
+    work) agrees with the model above on random and edge sizes, so the
+    coverage and workspace properties checked here hold for what it launches."""
+    import paged_quantized_kv_amd as pkv
+    rng = np.random.default_rng(5)
+    cases = [(200, 64, 8, 2560, 1024, 3072), (1, 8, 1, 1, 64, 3072), (4096, 64, 8, 4096, 64, 3072),
+             (4097, 64, 8, 4096, 64, 3072), (2, 1, 1, 700, 256, 3072), (2, 1, 1, 2000, 256, 3072),
+             (3, 16, 2, 1 << 30, 2048, 3072), (0, 8, 1, 100, 64, 3072), (10, 64, 8, 1024, 1024, 3072)]
+    for _ in range(3000):
+        kvh = int(rng.choice([1, 2, 4, 8, 16]))
+        cases.append((int(rng.integers(0, 5000)), kvh * int(rng.integers(1, 17)), kvh,
+                      int(rng.integers(0, 200000)), int(2 ** rng.integers(6, 12)),
+                      int(rng.choice([64, 1024, 3072, 7000]))))
+    for S, H, KVH, maxc, P, slots in cases:
+        want = balanced_units(S, H, KVH, maxc, P, slots) if S > 0 else 0
+        got = pkv.pkv_attention_balanced_units(S, H, KVH, maxc, P, slots)
+        assert got == want, (S, H, KVH, maxc, P, slots, got, want)
