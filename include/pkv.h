@@ -192,7 +192,13 @@ PKV_API int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride, int32_t
  *                   >= the side size H*B*(D/2 + D/16).
  *   slot_mapping    int64 [num_tokens].
  *   k_scale,
- *   v_scale         device binary32 scalars (the checkpoint scales).
+ *   v_scale         device binary32 scalars (the checkpoint scales), each a
+ *                   positive normal value, 2^-126 <= scale <= FLT_MAX, so
+ *                   that the global scale 1/scale is positive and finite.
+ *                   Zero, negative, subnormal or non-finite scales are
+ *                   outside the contract: the bytes written for them are
+ *                   unspecified (the addresses written are not affected).
+ *                   The value is read on the device, so it is not checked.
  *   head_size       multiple of 64 (so each 4x4 swizzle tile is complete);
  *   block_size      multiple of 4.
  */

@@ -1,6 +1,10 @@
 """Per-element error bound of the paged decode attention kernels against the
 exact (binary64) result, derived from their arithmetic.
 
+TEST INFRASTRUCTURE, like the rest of this package: the tests and
+``__graft_entry__.smoke()`` use it to judge the GPU result; the product
+never imports it.
+
 With w_t = exp(l_t - M) the exact softmax weights of the valid tokens,
 W = sum_t w_t, o = sum_t w_t v_t / W:
 

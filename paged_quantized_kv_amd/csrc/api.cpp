@@ -145,11 +145,11 @@ int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,
   // The page's own checks (head_size % 16, block_size % 4), plus head_size %
   // 64 so that every 4x4 swizzle tile of the V scales is complete.
   if (head_size % 16 != 0)
-    return fail(PKV_EUNSUPPORTED, "%s: head_size must be divisible by 16 for NVFP4 KV cache, got %d", op, head_size);
+    return fail(PKV_EUNSUPPORTED, "%s: head_size %d is not a multiple of 16 (16-element scale blocks)", op, head_size);
   if (head_size % 64 != 0)
-    return fail(PKV_EUNSUPPORTED, "%s: head_size must be a multiple of 64 for the V-scale swizzle, got %d", op, head_size);
+    return fail(PKV_EUNSUPPORTED, "%s: head_size %d is not a multiple of 64 (complete 4x4 V-scale swizzle tiles)", op, head_size);
   if (block_size % 4 != 0)
-    return fail(PKV_EUNSUPPORTED, "%s: block_size must be divisible by 4 for the NVFP4 swizzle, got %d", op, block_size);
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d is not a multiple of 4 (4-token swizzle tiles)", op, block_size);
   if (src_dtype != PKV_DTYPE_BF16 && src_dtype != PKV_DTYPE_F16)
     return fail(PKV_EINVAL, "%s: src_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, src_dtype);
   if (layout != PKV_LAYOUT_HND && layout != PKV_LAYOUT_NHD)
@@ -238,7 +238,7 @@ int pkv_gather_kv_fp4_dequant(const void* key_cache, const void* value_cache, vo
   if (head_size % 64 != 0)
     return fail(PKV_EUNSUPPORTED, "%s: head_size must be a multiple of 64, got %d", op, head_size);
   if (block_size % 4 != 0)
-    return fail(PKV_EUNSUPPORTED, "%s: block_size must be divisible by 4, got %d", op, block_size);
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d is not a multiple of 4 (4-token swizzle tiles)", op, block_size);
   if (out_dtype != PKV_DTYPE_BF16 && out_dtype != PKV_DTYPE_F16)
     return fail(PKV_EINVAL, "%s: out_dtype must be PKV_DTYPE_BF16 or PKV_DTYPE_F16, got %d", op, out_dtype);
   if (layout != PKV_LAYOUT_HND && layout != PKV_LAYOUT_NHD)

@@ -128,9 +128,9 @@ def store4(**kw):
 
 
 @pytest.mark.parametrize("kw,code,msg", [
-    (dict(D=40, kst=320, vst=320), PKV_EUNSUPPORTED, "divisible by 16"),
+    (dict(D=40, kst=320, vst=320), PKV_EUNSUPPORTED, "not a multiple of 16"),
     (dict(D=96, kst=768, vst=768), PKV_EUNSUPPORTED, "multiple of 64"),
-    (dict(B=6), PKV_EUNSUPPORTED, "divisible by 4"),
+    (dict(B=6), PKV_EUNSUPPORTED, "not a multiple of 4"),
     (dict(layout=2), PKV_EINVAL, "layout"),
     (dict(kst=1000), PKV_EINVAL, "row strides"),
     (dict(kst=1028), PKV_EALIGN, "multiples of 8"),
@@ -193,7 +193,7 @@ def g4(**kw):
 
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(D=96, kst=768, vst=768), PKV_EUNSUPPORTED, "multiple of 64"),
-    (dict(B=6), PKV_EUNSUPPORTED, "divisible by 4"),
+    (dict(B=6), PKV_EUNSUPPORTED, "not a multiple of 4"),
     (dict(layout=2), PKV_EINVAL, "layout"),
     (dict(dt=5), PKV_EINVAL, "out_dtype"),
     (dict(kst=1000), PKV_EINVAL, "row strides"),

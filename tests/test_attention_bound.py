@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads
-from attention_bound import attention_bound, emulate_f32
+from oracle.attention_bound import attention_bound, emulate_f32
 
 
 def case(seed=3, lens=(1, 17, 300, 1000), H=8, KVH=2, B=16):

@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from attention_bound import attention_bound
+from oracle.attention_bound import attention_bound
 from test_attention_split import balanced_units
 
 pytestmark = pytest.mark.gpu

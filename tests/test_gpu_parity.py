@@ -291,7 +291,10 @@ def test_store_fp4_value_edge_cases():
 def test_store_fp4_prefill_sampled():
     """256 x 1000-token prefill batch, H=8, D=128, B=16 (the benchmark's shape):
     full GPU run; the oracle recomputes 3000 sampled tokens and every byte those
-    tokens own is compared, plus the K and V scale regions of their pages."""
+    tokens own is compared: their code bytes and their K and V scale bytes.
+    The owned bytes are found without any layout formula: the oracle runs
+    twice, over the sentinel cache and over its bitwise complement, and the
+    bytes that come out equal in both runs are the ones the tokens write."""
     f = workloads.prefill_fp4()
     banner(f"nvfp4 {f.name} sampled")
     c = dev(f.cache_init)
@@ -304,21 +307,42 @@ def test_store_fp4_prefill_sampled():
                          block_size=f.block_size, layout=f.layout)
     got = host(c)
     pick = np.sort(workloads.rng(5).choice(T, size=3000, replace=False))
-    ref = f.cache_init.copy()
-    oracle.store_kv_fp4(np.ascontiguousarray(f.key_bits[pick]),
-                        np.ascontiguousarray(f.value_bits[pick]), ref,
-                        np.ascontiguousarray(f.slot_mapping[pick]), f.num_heads, f.head_size,
-                        f.block_size, f.layout, f.k_scale, f.v_scale)
-    owned = ref != f.cache_init           # bytes the sampled tokens changed
-    # plus every byte they own that happens to equal the sentinel: the data rows
-    H, D, B = f.num_heads, f.head_size, f.block_size
-    for slot in f.slot_mapping[pick]:
-        p, off = divmod(int(slot), B)
-        for h in range(H):
-            a = (h * B + off) * (D // 2)
-            owned[p, :, a:a + D // 2] = True
-    assert owned.sum() > 3000 * 2 * H * D // 2
-    np.testing.assert_array_equal(got[owned], ref[owned])
+    refs = []
+    for init in (f.cache_init, ~f.cache_init):
+        ref = init.copy()
+        oracle.store_kv_fp4(np.ascontiguousarray(f.key_bits[pick]),
+                            np.ascontiguousarray(f.value_bits[pick]), ref,
+                            np.ascontiguousarray(f.slot_mapping[pick]), f.num_heads,
+                            f.head_size, f.block_size, f.layout, f.k_scale, f.v_scale)
+        refs.append(ref)
+    owned = refs[0] == refs[1]
+    H, D = f.num_heads, f.head_size
+    kept = int((f.slot_mapping[pick] >= 0).sum())
+    # per token: H*D/2 code bytes and H*D/16 scale bytes on each of two sides
+    assert owned.sum() == kept * 2 * H * (D // 2 + D // 16)
+    np.testing.assert_array_equal(got[owned], refs[0][owned])
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(2.0 ** -126, 3.4028234663852886e38),
+                                             (3.4028234663852886e38, 2.0 ** -126)])
+def test_store_fp4_global_scale_domain_ends(k_scale, v_scale):
+    """The two ends of the scales the boundary accepts (positive normal
+    binary32): 2^-126 gives the global scale 2^126, FLT_MAX a subnormal one.
+    Blocks span every bf16 binade, with zero and negative-zero blocks, so the
+    products amax * gs overflow, underflow and land in between."""
+    banner(f"nvfp4 k_scale = {k_scale:g}, v_scale = {v_scale:g}")
+    g = workloads.rng(29)
+    T, H, D, B = 48, 2, 128, 16
+
+    def src():
+        x = g.standard_normal((T, H, D // 16, 16)).astype(np.float32)
+        x *= np.exp2(g.integers(-140, 126, size=(T, H, D // 16, 1))).astype(np.float32)
+        x[:, :, 0] = 0.0                    # all-zero blocks
+        x[:, 0, 1] = -0.0                   # negative-zero blocks
+        return x.reshape(T, H, D)
+
+    f = _fp4_custom(src(), src(), B, k_scale, v_scale)
+    run_store4(f)
 
 
 # ---------------------------------------------------------------- codecs
