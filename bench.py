@@ -21,28 +21,31 @@ store wrote at step i - 4, so no kernel reads data that the 256 MB Infinity
 Cache still holds from a recent write; the NVFP4 store reads 1 GB of K/V and
 writes 0.3 GB of pages per step.
 
-After the timed steps, the reader side is timed on the same batch (not part
-of `value`): pkv_gather_indexer_k_dequant (indexer pages -> bf16 rows) and
-pkv_gather_kv_fp4_dequant (NVFP4 pages -> bf16 K and V rows), reported under
-`reader_side`.
-
-Then the decode consumer of fp8 KV pages is timed on its own batch (not
-part of `value` either): pkv_paged_attention_decode over one decode step of
-200 requests with Llama-3.1-70B attention shapes (64 query heads, 8 KV heads,
-head size 128, 16-token pages, contexts uniform in [128, 2560]: 0.5 GB of K/V
-codes), reported under `decode_attention`.
-
-Printed: one JSON line.  `value` = algorithmic bytes of one step / measured
-step time (GB/s), the wall clock of K steps with nothing between the
-launches; the per-kernel durations come from the K steps that follow, with
-HIP events recorded on the launch stream around each launch (timing-only
-events, without the cache write-back a default event performs), and
-`ms_per_step_with_events` is those steps' wall clock; `roofline` describes
-the kernel with the longest average duration; `d2d_copy_same_bytes` times a
-device-to-device copy moving the step's bytes (the practical ceiling);
-`store_kv_fp4_alone` times the NVFP4 store back to back with the
-workload's slots and with the same tokens stored to pages in order;
-`cpu_baseline` times the CPU oracle on the same batch (one thread).
+Timing, in this order:
+  - pre-roll: steps launched for a fixed 0.5 s of wall clock (reported as
+    `preroll`, not counted in `warmup`), so that the clocks have left their
+    idle state before anything is timed;
+  - `warmup` untimed steps, then `steps` steps timed by wall clock between
+    two synchronizations, nothing recorded between the launches:
+    `ms_per_step` and `value`;
+  - each of the step's three kernels alone: 32 launches back to back (the
+    same rotating buffers) between one pair of HIP events on the launch
+    stream, three times, median of the three averages: `kernels`;
+    `roofline` describes the kernel with the longest duration;
+  - reported workloads (not part of `value`): the gather on 8 long ragged
+    requests, the 16 x 512-token store-then-gather round trip and the NVFP4
+    store of [4096, 8, 128] K and V, each timed the same way;
+  - the reader side (pkv_gather_indexer_k_dequant, pkv_gather_kv_fp4_dequant)
+    on the prefill batch and the decode consumer (pkv_paged_attention_decode,
+    200 requests with Llama-3.1-70B attention shapes) on its own batch, timed
+    the same way;
+  - `d2d_copy_same_bytes`: the runtime's device-to-device copy moving the
+    step's bytes (a practical ceiling);
+  - `cpu_baseline`: the CPU oracle on bounded samples of the same batch, per
+    op, on one thread and on every thread used (the oracle's functions called
+    on disjoint token or request ranges), median of 5 after one warm-up.
+Events are created with hipEventDisableSystemFence (recording one then does
+not write back and invalidate the caches).  Printed: one JSON line.
 """
 from __future__ import annotations
 
@@ -51,6 +54,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -60,8 +64,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 METRIC = "gather/store HBM GB/s and % of MI355X peak; Mtokens/s at 256×1000 tok"
+PREROLL_S = 0.5                 # fixed pre-roll of step launches before any timing
+B2B_LAUNCHES = 32               # back-to-back launches per timed kernel run
+B2B_RUNS = 3                    # runs per kernel; the median is reported
 
 CSRC = os.path.join(ROOT, "paged_quantized_kv_amd", "csrc")
+BUILD_PY = os.path.join(ROOT, "paged_quantized_kv_amd", "build.py")
 KERNEL_SOURCES = {
     "store_indexer_k_fp8": ["store_indexer_k_fp8.hip", "device_common.h"],
     "store_kv_fp4": ["store_kv_fp4.hip", "device_common.h"],
@@ -74,10 +82,14 @@ PROFILES = os.path.join(ROOT, "profiles")
 
 
 def source_hash(kernel: str) -> str:
+    """Hash of the kernel's source files and of the build script (its flags
+    shape the compiled kernel too)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
+    with open(BUILD_PY, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 
@@ -99,14 +111,12 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--sets", type=int, default=8, help="rotating indexer buffer sets")
     p.add_argument("--no-cpu-baseline", action="store_true",
                    help="skip the CPU oracle timing (profiling runs)")
-    p.add_argument("--reader-steps", type=int, default=50,
-                   help="timed iterations of the reader-side gathers (0: skip them)")
-    p.add_argument("--decode-steps", type=int, default=50,
-                   help="timed calls of the paged decode attention (0: skip them)")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time only the step and its three kernels (short profiling runs)")
     p.add_argument("--calibration-copy", action="store_true",
                    help="run a plain 256 MiB fp32 copy-like kernel (torch.neg) before the "
                         "timed steps, for scaling hardware byte counters")
@@ -118,8 +128,7 @@ class HipTimingEvents:
 
     They are created with hipEventDisableSystemFence: recording one then does
     not write back and invalidate the caches, which torch's events do and
-    which would add that cost to the kernel timed before it and to the one
-    after it.  A timed step therefore runs like an untimed one."""
+    which would add that cost to the kernels around it."""
 
     DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence
 
@@ -143,7 +152,6 @@ class HipTimingEvents:
                    "hipEventDestroy"):
             getattr(hip, fn).restype = ctypes.c_int
         self._hip = hip
-        self._events = []
 
     def _ok(self, rc, what):
         if rc != 0:
@@ -153,7 +161,6 @@ class HipTimingEvents:
         ev = self._ct.c_void_p()
         self._ok(self._hip.hipEventCreateWithFlags(self._ct.byref(ev), self.DISABLE_SYSTEM_FENCE),
                  "hipEventCreateWithFlags")
-        self._events.append(ev)
         return ev
 
     def record(self, ev, stream_handle):
@@ -164,10 +171,39 @@ class HipTimingEvents:
         self._ok(self._hip.hipEventElapsedTime(self._ct.byref(ms), a, b), "hipEventElapsedTime")
         return ms.value
 
-    def destroy_all(self):
-        for ev in self._events:
+    def destroy(self, *events):
+        for ev in events:
             self._hip.hipEventDestroy(ev)
-        self._events = []
+
+
+def time_back_to_back(torch, timing, stream, launch, n=B2B_LAUNCHES, runs=B2B_RUNS):
+    """Median over `runs` of the average duration (ms) of `n` launches issued
+    back to back between one pair of events on the launch stream; launch(i)
+    enqueues the i-th launch."""
+    e0, e1 = timing.create(), timing.create()
+    for i in range(4):
+        launch(i)
+    torch.cuda.synchronize()
+    avgs = []
+    for r in range(runs):
+        timing.record(e0, stream)
+        for i in range(n):
+            launch(r * n + i)
+        timing.record(e1, stream)
+        torch.cuda.synchronize()
+        avgs.append(timing.elapsed_ms(e0, e1) / n)
+    timing.destroy(e0, e1)
+    return statistics.median(avgs)
+
+
+def rate(nbytes, tokens, ms):
+    """GB/s, fraction of the HBM peak and Mtokens/s of `nbytes` and `tokens` per `ms`."""
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    out = {"us": round(ms * 1e3, 2), "alg_bytes": int(nbytes), "GBps": round(gbps, 1),
+           "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+    if tokens is not None:
+        out["mtokens_per_s"] = round(tokens / (ms * 1e-3) / 1e6, 1)
+    return out
 
 
 def algorithmic_bytes(T, D, H4, D4, R, maxb):
@@ -178,97 +214,34 @@ def algorithmic_bytes(T, D, H4, D4, R, maxb):
     return {"store_indexer_k_fp8": store8, "store_kv_fp4": fp4, "gather_indexer_k_fp8": gather}
 
 
+def gather_bytes(w):
+    """Gather bytes of an indexer workload: 2 (D + 4) per token, table and cu_seq_lens."""
+    R, maxb = w.block_table.shape
+    return w.num_tokens * 2 * (w.head_dim + 4) + R * maxb * 4 + (R + 1) * 4
+
+
+def store8_bytes(w):
+    """fp8 store bytes of an indexer workload: bf16 row and slot read, codes and
+    scale written for every token with a slot."""
+    T, D = w.k_bits.shape[0], w.head_dim
+    kept = int((w.slot_mapping >= 0).sum())
+    return T * (2 * D + 8) + kept * (D + 4)
+
+
+def fp4_bytes(f):
+    """NVFP4 store bytes: K and V 16-bit rows and the slot read for every token,
+    code and scale bytes of both sides written for every token with a slot."""
+    T = f.slot_mapping.shape[0]
+    H, D = f.num_heads, f.head_size
+    kept = int((f.slot_mapping >= 0).sum())
+    return T * (2 * H * D * 2 + 8) + kept * 2 * H * (D // 2 + D // 16) + 8
+
+
 def reader_bytes(T, D, H4, D4, R, maxb, R4, maxb4):
     """Bytes the reader-side gathers must move (read + write) over the batch."""
     idx = T * (D + 4 + 2 * D) + R * maxb * 4 + (R + 1) * 4      # codes + scale -> bf16 row
     fp4 = T * 2 * H4 * (D4 // 2 + D4 // 16 + 2 * D4) + R4 * maxb4 * 4 + (R4 + 1) * 4 + 8
     return {"gather_indexer_k_dequant": idx, "gather_kv_fp4_dequant": fp4}
-
-
-def cpu_baseline(w, f, step_bytes):
-    import numpy as np
-
-    import oracle
-    cache = w.cache_init.copy()
-    kf, ks = w.k_fp8_init.copy(), w.k_scale_init.copy()
-    c4 = f.cache_init.copy()
-    t0 = time.perf_counter()
-    oracle.store_indexer_k_fp8(w.k_bits, w.slot_mapping, cache, w.block_size, w.head_dim)
-    oracle.store_kv_fp4(f.key_bits, f.value_bits, c4, f.slot_mapping, f.num_heads, f.head_size,
-                        f.block_size, f.layout, f.k_scale, f.v_scale)
-    oracle.gather_indexer_k_fp8(cache, kf, ks, w.block_table, w.cu_seq_lens, w.block_size,
-                                w.head_dim)
-    dt = time.perf_counter() - t0
-    del np
-    return {"value": round(step_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "seconds": round(dt, 3),
-            "mtokens_per_s": round(w.num_tokens / dt / 1e6, 4),
-            "sample": "one full step (256 req x 1000 tok through fp8 store, NVFP4 store and "
-                      "gather), plain C oracle, one thread"}
-
-
-def time_reader(args, pkv, torch, timing, stream, sets, w, f, bt, cu, c4, k4s, v4s):
-    """Average durations (ms) of the two reader-side gathers over the batch,
-    timed like the step's kernels.  The indexer read-back cycles over the
-    rotating page sets; the NVFP4 read-back reads the pages the last step
-    stored (0.3 GB, larger than the Infinity Cache)."""
-    T = w.num_tokens
-    H4, D4 = f.num_heads, f.head_size
-    outs = [torch.empty((T, w.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
-    ko = torch.empty((T, H4, D4), dtype=torch.bfloat16, device="cuda")
-    vo = torch.empty((T, H4, D4), dtype=torch.bfloat16, device="cuda")
-    bt4, cu4 = (torch.from_numpy(a).to("cuda") for a in (f.block_table, f.cu_seq_lens))
-    names = ["gather_indexer_k_dequant", "gather_kv_fp4_dequant"]
-
-    def it(i, ev=None):
-        s = sets[i % len(sets)]
-        if ev is not None:
-            timing.record(ev[0], stream)
-        pkv.pkv_gather_indexer_k_dequant(s["cache"], outs[i % 2], bt, cu, block_size=w.block_size)
-        if ev is not None:
-            timing.record(ev[1], stream)
-        pkv.pkv_gather_kv_fp4_dequant(c4[:, 0], c4[:, 1], ko, vo, bt4, cu4, k4s, v4s,
-                                      block_size=f.block_size, layout=f.layout)
-        if ev is not None:
-            timing.record(ev[2], stream)
-
-    evs = [[timing.create() for _ in range(3)] for _ in range(args.reader_steps)]
-    for i in range(min(args.warmup, 20)):
-        it(i)
-    torch.cuda.synchronize()
-    for i in range(args.reader_steps):
-        it(i, evs[i])
-    torch.cuda.synchronize()
-    ms = {n: sum(timing.elapsed_ms(e[j], e[j + 1]) for e in evs) / args.reader_steps
-          for j, n in enumerate(names)}
-    del outs, ko, vo
-    timing.destroy_all()
-    return ms
-
-
-def time_d2d_copy(torch, timing, stream, nbytes, reps=20):
-    """A device-to-device copy (torch's copy_, the runtime's copy kernel)
-    moving nbytes in all (half read, half written): the practical ceiling
-    the step's kernels are set against."""
-    half = (nbytes // 2 + 255) // 256 * 256
-    src = torch.empty(half, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    e0, e1 = timing.create(), timing.create()
-    timing.record(e0, stream)
-    for _ in range(reps):
-        dst.copy_(src)
-    timing.record(e1, stream)
-    torch.cuda.synchronize()
-    ms = timing.elapsed_ms(e0, e1) / reps
-    timing.destroy_all()
-    del src, dst
-    gbps = 2 * half / (ms * 1e-3) / 1e9
-    return {"bytes": 2 * half, "us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-            "what": "torch copy_ of half the step's algorithmic bytes (read + write = the step's bytes)"}
 
 
 def decode_attention_bytes(c):
@@ -282,11 +255,217 @@ def decode_attention_bytes(c):
     return kv + 2 * (S * H * D * 2) + 4 * int(sum(-(-n // B) for n in L)) + 4 * S
 
 
-def time_decode_attention(args, pkv, torch, timing, stream, workloads, np):
-    """Average duration (ms) of one pkv_paged_attention_decode call (partition
-    and reduce kernels) over the decode batch, timed like the step's kernels.
-    Its 0.5 GB of K/V codes is larger than the Infinity Cache, so each call
-    reads them from HBM."""
+def rotation_sets(footprint_bytes, cap=8):
+    """Buffer sets to rotate so that the sets together exceed twice the 256 MB
+    Infinity Cache (at least one)."""
+    return max(1, min(cap, -(-(512 << 20) // max(1, footprint_bytes))))
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_threads():
+    """Threads the CPU baseline uses: every host CPU, but no more than the
+    OMP_NUM_THREADS share when that is set."""
+    n = os.cpu_count() or 1
+    share = os.environ.get("OMP_NUM_THREADS")
+    if share and share.isdigit() and int(share) > 0:
+        n = min(n, int(share))
+    return n
+
+
+def _split(n, parts):
+    step = -(-n // parts)
+    return [(a, min(a + step, n)) for a in range(0, n, step)]
+
+
+def oracle_ops(w, f, fp4_sample_tokens):
+    """The oracle's three step ops on fresh copies of the sentinel buffers,
+    each as (fn(a, b), n, algorithmic bytes, tokens, sample, outputs): fn runs
+    the oracle on items [a, b) (tokens for the stores, requests for the
+    gather), so calls on disjoint ranges write disjoint bytes."""
+    import oracle
+    T, D = w.num_tokens, w.head_dim
+    R = w.block_table.shape[0]
+    n4 = min(fp4_sample_tokens, f.slot_mapping.shape[0])
+    H4, D4 = f.num_heads, f.head_size
+    cache8 = w.cache_init.copy()
+    kf, ks = w.k_fp8_init.copy(), w.k_scale_init.copy()
+    c4 = f.cache_init.copy()
+
+    def store8(a, b):
+        oracle.store_indexer_k_fp8(w.k_bits[a:b], w.slot_mapping[a:b], cache8, w.block_size, D,
+                                   dtype=w.dtype)
+
+    def gather(a, b):
+        oracle.gather_indexer_k_fp8(cache8, kf, ks, w.block_table[a:b], w.cu_seq_lens[a:b + 1],
+                                    w.block_size, D)
+
+    def store4(a, b):
+        oracle.store_kv_fp4(f.key_bits[a:b], f.value_bits[a:b], c4, f.slot_mapping[a:b],
+                            f.num_heads, f.head_size, f.block_size, f.layout, f.k_scale,
+                            f.v_scale, dtype=f.dtype)
+
+    return {
+        "store_indexer_k_fp8": (store8, T, T * (2 * D + 8 + D + 4), T,
+                                f"{T} tokens (the whole batch)", [cache8]),
+        "store_kv_fp4": (store4, n4, n4 * (2 * H4 * D4 * 2 + 8 + 2 * H4 * (D4 // 2 + D4 // 16)),
+                         n4, f"the first {n4} tokens", [c4]),
+        "gather_indexer_k_fp8": (gather, R, T * 2 * (D + 4) + w.block_table.size * 4 + (R + 1) * 4,
+                                 T, f"{T} tokens (the whole batch)", [kf, ks]),
+    }
+
+
+def run_split(pool, fn, n, threads):
+    """fn over [0, n) on one thread, or over `threads` disjoint ranges on the pool."""
+    if threads == 1:
+        fn(0, n)
+    else:
+        list(pool.map(lambda ab: fn(*ab), _split(n, threads)))
+
+
+def cpu_baseline(w, f, fp4_sample_tokens=16000, runs=5):
+    """The oracle as it stands, on bounded samples of the prefill batch: every
+    op on one thread and on `cpu_threads()` threads (disjoint token ranges for
+    the stores, disjoint request ranges for the gather; ctypes releases the
+    GIL during each call), median of `runs` after one warm-up."""
+    from concurrent.futures import ThreadPoolExecutor
+    nthreads = cpu_threads()
+    pool = ThreadPoolExecutor(nthreads)
+    ops = oracle_ops(w, f, fp4_sample_tokens)
+
+    def timed(fn, n, threads):
+        t0 = time.perf_counter()
+        run_split(pool, fn, n, threads)
+        return time.perf_counter() - t0
+
+    out = {}
+    total_bytes = 0
+    total_s_all = 0.0
+    for name, (fn, n, nbytes, tokens, what, _) in ops.items():
+        entry = {"sample": what}
+        for label, threads in (("one_thread", 1), ("all_threads", nthreads)):
+            timed(fn, n, threads)                        # warm-up
+            s = statistics.median(timed(fn, n, threads) for _ in range(runs))
+            entry[label] = {"threads": threads, "seconds": round(s, 4),
+                            "GBps": round(nbytes / s / 1e9, 4),
+                            "mtokens_per_s": round(tokens / s / 1e6, 4)}
+        out[name] = entry
+        total_bytes += nbytes
+        total_s_all += entry["all_threads"]["seconds"]
+    pool.shutdown()
+    n4 = ops["store_kv_fp4"][1]
+    return {"value": round(total_bytes / total_s_all / 1e9, 4), "unit": "GB/s",
+            "cores": nthreads, "host_cpu_count": os.cpu_count(), "kind": "oracle",
+            "sample": (f"per op: fp8 store and gather on the whole 256 x 1000-token batch, "
+                       f"NVFP4 store on its first {n4} tokens; value = the samples' algorithmic "
+                       f"bytes over their summed times on {nthreads} threads (median of "
+                       f"{runs} after one warm-up)"),
+            "ops": out}
+
+
+# ---------------------------------------------------------------- reported workloads
+def time_reported(torch, np, pkv, workloads, timing, stream):
+    """The long ragged gather, the round-trip store + gather and the NVFP4
+    store of [4096, 8, 128] K and V, each launched back to back."""
+    def to(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+    out = {}
+    # long ragged gather: 8 requests of up to 32768 tokens, 8192 pages
+    w = workloads.c3_long_ragged()
+    T = w.num_tokens
+    nsets = rotation_sets(w.cache_init.nbytes + T * (w.head_dim + 4))
+    sets = [(to(w.cache_init), to(w.k_fp8_init), to(w.k_scale_init)) for _ in range(nsets)]
+    bt, cu = to(w.block_table), to(w.cu_seq_lens)
+
+    def g3(i):
+        c, kf, ks = sets[i % nsets]
+        pkv.pkv_gather_indexer_k_fp8(c, kf, ks, bt, cu, block_size=w.block_size)
+
+    ms = time_back_to_back(torch, timing, stream, g3)
+    out["gather_long_ragged"] = dict(rate(gather_bytes(w), T, ms), rotating_sets=nsets,
+                                     workload=f"8 requests, {T} tokens (lengths "
+                                              f"{[int(x) for x in w.lens]}), B=64, D=128, "
+                                              "8192 pages")
+    del sets
+    # round trip: fp8 store of 8192 tokens (5% slots -1), then gather of 16 x 512
+    w = workloads.c4_roundtrip()
+    T = w.num_tokens
+    nsets = rotation_sets(w.cache_init.nbytes + T * (w.head_dim * 3 + 4))
+    sets = [(to(w.k_bits.view(np.int16)).view(torch.bfloat16), to(w.cache_init),
+             to(w.k_fp8_init), to(w.k_scale_init)) for _ in range(nsets)]
+    slots, bt, cu = to(w.slot_mapping), to(w.block_table), to(w.cu_seq_lens)
+
+    def s4(i):
+        k, c, _, _ = sets[i % nsets]
+        pkv.pkv_store_indexer_k_fp8(k, slots, c, block_size=w.block_size)
+
+    def g4(i):
+        _, c, kf, ks = sets[i % nsets]
+        pkv.pkv_gather_indexer_k_fp8(c, kf, ks, bt, cu, block_size=w.block_size)
+
+    ms_s, ms_g = (time_back_to_back(torch, timing, stream, fn) for fn in (s4, g4))
+    out["roundtrip_store"] = dict(rate(store8_bytes(w), T, ms_s), rotating_sets=nsets,
+                                  workload="16 x 512 tokens, D=128, 256 pages of 64, "
+                                           "5% of slots -1")
+    out["roundtrip_gather"] = dict(rate(gather_bytes(w), T, ms_g), rotating_sets=nsets,
+                                   workload="the same pages gathered back, 16 x 512 tokens")
+    del sets
+    # NVFP4 store: K and V [4096, 8, 128], B=16, 512 pages, 5% of slots -1, HND
+    f = workloads.c5_nvfp4_store(0)
+    T = f.slot_mapping.shape[0]
+    nsets = rotation_sets(f.cache_init.nbytes + f.key_bits.nbytes * 2)
+    shape = (T, f.num_heads, f.head_size)
+    sets = [(to(f.key_bits.view(np.int16)).view(torch.bfloat16).view(shape),
+             to(f.value_bits.view(np.int16)).view(torch.bfloat16).view(shape),
+             to(f.cache_init)) for _ in range(nsets)]
+    sl = to(f.slot_mapping)
+    ksc = torch.tensor([f.k_scale], dtype=torch.float32, device="cuda")
+    vsc = torch.tensor([f.v_scale], dtype=torch.float32, device="cuda")
+
+    def s5(i):
+        k, v, c = sets[i % nsets]
+        pkv.pkv_store_kv_fp4(k, v, c[:, 0], c[:, 1], sl, ksc, vsc, block_size=f.block_size,
+                             layout=0)
+
+    ms = time_back_to_back(torch, timing, stream, s5)
+    out["nvfp4_store_4096x8x128"] = dict(rate(fp4_bytes(f), T, ms), rotating_sets=nsets,
+                                         workload="K and V [4096, 8, 128] bf16, B=16, 512 pages, "
+                                                  "HND, 5% of slots -1")
+    del sets
+    return out
+
+
+def time_reader(torch, np, pkv, timing, stream, sets, w, f, bt, cu, c4, k4s, v4s):
+    """Durations (ms) of the two reader-side gathers over the batch, each
+    launched back to back.  The indexer read-back cycles over the rotating
+    page sets; the NVFP4 read-back reads the pages of the step's NVFP4 store
+    (0.3 GB, larger than the Infinity Cache)."""
+    T = w.num_tokens
+    H4, D4 = f.num_heads, f.head_size
+    outs = [torch.empty((T, w.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ko = torch.empty((T, H4, D4), dtype=torch.bfloat16, device="cuda")
+    vo = torch.empty((T, H4, D4), dtype=torch.bfloat16, device="cuda")
+    bt4, cu4 = (torch.from_numpy(a).to("cuda") for a in (f.block_table, f.cu_seq_lens))
+
+    def idx(i):
+        pkv.pkv_gather_indexer_k_dequant(sets[i % len(sets)]["cache"], outs[i % 2], bt, cu,
+                                         block_size=w.block_size)
+
+    def fp4(i):
+        pkv.pkv_gather_kv_fp4_dequant(c4[:, 0], c4[:, 1], ko, vo, bt4, cu4, k4s, v4s,
+                                      block_size=f.block_size, layout=f.layout)
+
+    ms = {"gather_indexer_k_dequant": time_back_to_back(torch, timing, stream, idx),
+          "gather_kv_fp4_dequant": time_back_to_back(torch, timing, stream, fp4)}
+    del outs, ko, vo
+    return ms
+
+
+def time_decode_attention(torch, np, pkv, workloads, timing, stream):
+    """Duration of one pkv_paged_attention_decode call (partition and reduce
+    kernels) over the decode batch, launched back to back.  Its 0.5 GB of K/V
+    codes is larger than the Infinity Cache, so each call reads them from
+    HBM."""
     c = workloads.decode_batch()
     S, H, D = c.query.shape
     B = c.key_cache.shape[3]
@@ -301,30 +480,39 @@ def time_decode_attention(args, pkv, torch, timing, stream, workloads, np):
     P = workloads.DECODE_PARTITION
     ws = pkv.paged_attention_workspace(S, H, maxc, P, device="cuda")
 
-    def call():
+    def call(i):
         pkv.pkv_paged_attention_decode(out, *ws, q, kc, vc, c.num_kv_heads, c.scale, bt, cl, B,
                                        maxc, c.k_scale, c.v_scale, partition_size=P)
 
-    evs = [[timing.create() for _ in range(2)] for _ in range(args.decode_steps)]
-    for _ in range(min(args.warmup, 20)):
-        call()
-    torch.cuda.synchronize()
-    for e in evs:
-        timing.record(e[0], stream)
-        call()
-        timing.record(e[1], stream)
-    torch.cuda.synchronize()
-    ms = sum(timing.elapsed_ms(e[0], e[1]) for e in evs) / args.decode_steps
-    timing.destroy_all()
+    ms = time_back_to_back(torch, timing, stream, call)
     nbytes = decode_attention_bytes(c)
-    gbps = nbytes / (ms * 1e-3) / 1e9
-    return {"us": round(ms * 1e3, 2), "alg_bytes": nbytes, "GBps": round(gbps, 1),
-            "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-            "seqs_per_s": round(S / (ms * 1e-3), 1),
-            "context_tokens": int(c.context_lens.sum()),
-            "workload": "decode step: 200 req, H=64, KVH=8, D=128, B=16, contexts U[128, 2560], "
-                        f"fp8 E4M3 K/V, partitions of {P}",
-            "traffic": measured_traffic("paged_attention_decode", "decode_200req")}
+    res = rate(nbytes, None, ms)
+    res.update({"seqs_per_s": round(S / (ms * 1e-3), 1),
+                "context_tokens": int(c.context_lens.sum()),
+                "workload": "decode step: 200 req, H=64, KVH=8, D=128, B=16, contexts "
+                            f"U[128, 2560], fp8 E4M3 K/V, partitions of {P}",
+                "traffic": measured_traffic("paged_attention_decode", "decode_200req")})
+    return res
+
+
+def time_d2d_copy(torch, timing, stream, nbytes):
+    """A device-to-device copy (torch's copy_, the runtime's copy kernel)
+    moving nbytes in all (half read, half written), over rotating buffers."""
+    half = (nbytes // 2 + 255) // 256 * 256
+    nsets = rotation_sets(2 * half, cap=4)
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(nsets)]
+
+    def cp(i):
+        src, dst = bufs[i % nsets]
+        dst.copy_(src)
+
+    ms = time_back_to_back(torch, timing, stream, cp, n=12)
+    del bufs
+    res = rate(2 * half, None, ms)
+    res["what"] = ("torch copy_ of half the step's algorithmic bytes (read + write = the step's "
+                   "bytes), back to back over rotating buffers")
+    return res
 
 
 def main():
@@ -376,28 +564,28 @@ def main():
     torch.cuda.synchronize()
 
     names = ["store_indexer_k_fp8", "store_kv_fp4", "gather_indexer_k_fp8"]
-
     lag = len(sets) // 2  # the gather reads pages stored `lag` steps earlier
 
     timing = HipTimingEvents()
     stream = torch.cuda.current_stream().cuda_stream  # every launch goes to this stream
 
-    def mark(ev, j):
-        if ev is not None:
-            timing.record(ev[j], stream)
-
-    def step(i, ev=None):
+    def store8(i):
         s = sets[i % len(sets)]
-        sg = sets[(i - lag) % len(sets)]
-        mark(ev, 0)
         pkv.pkv_store_indexer_k_fp8(s["k"], s["slot"], s["cache"], block_size=w.block_size)
-        mark(ev, 1)
+
+    def store4(i):
         pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slot4, k4s, v4s,
                              block_size=f.block_size, layout=f.layout)
-        mark(ev, 2)
+
+    def gather(i):
+        sg = sets[(i - lag) % len(sets)]
         pkv.pkv_gather_indexer_k_fp8(sg["cache"], sg["kf"], sg["ks"], bt, cu,
                                      block_size=w.block_size)
-        mark(ev, 3)
+
+    def step(i):
+        store8(i)
+        store4(i)
+        gather(i)
 
     if args.calibration_copy:
         src = torch.randn(64 << 20, device=dev)          # 256 MiB fp32
@@ -407,105 +595,42 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # Events are created before the warmup so that no host-side pause separates
-    # the warmup from the timed steps (an idle GPU lowers its clocks).  The
-    # default warmup (~30 ms of steps) runs past the clock transient that the
-    # first few dozen launches of the step show, so the timed steps measure the
-    # sustained rate.
-    # The step's wall clock is taken over K steps with no event between
-    # launches (each recorded event is one more packet the command processor
-    # waits on, about 2 us per event here); the per-kernel durations come
-    # from the next K steps, with events around every launch.
-    events = [[timing.create() for _ in range(4)] for _ in range(args.steps)]
+    # fixed pre-roll: steps for PREROLL_S of wall clock, in batches of 20
+    t_pre = time.perf_counter()
+    preroll_steps = 0
+    while time.perf_counter() - t_pre < PREROLL_S:
+        for _ in range(20):
+            step(preroll_steps)
+            preroll_steps += 1
+        torch.cuda.synchronize()
+    preroll_s = time.perf_counter() - t_pre
+
     for i in range(args.warmup):
-        step(i)
+        step(preroll_steps + i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    base = preroll_steps + args.warmup
     for i in range(args.steps):
-        step(args.warmup + i)
+        step(base + i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t1 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + args.steps + i, events[i])
-    torch.cuda.synchronize()
-    wall_events = time.perf_counter() - t1
-
-    per_kernel_ms = {n: 0.0 for n in names}
-    for ev in events:
-        for j, n in enumerate(names):
-            per_kernel_ms[n] += timing.elapsed_ms(ev[j], ev[j + 1])
-    per_kernel_ms = {n: v / args.steps for n, v in per_kernel_ms.items()}
-    timing.destroy_all()
     ms_per_step = wall * 1e3 / args.steps
 
-    reader = None
-    if args.reader_steps > 0:
-        reader = time_reader(args, pkv, torch, timing, stream, sets, w, f, bt, cu, c4, k4s, v4s)
-        R4, maxb4 = f.block_table.shape
-        rb = reader_bytes(T, D, H4, D4, R, maxb, R4, maxb4)
-        reader = {n: {"us": round(reader[n] * 1e3, 2), "alg_bytes": rb[n],
-                      "GBps": round(rb[n] / (reader[n] * 1e-3) / 1e9, 1),
-                      "frac_hbm_peak": round(rb[n] / (reader[n] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "mtokens_per_s": round(T / (reader[n] * 1e-3) / 1e6, 1),
-                      "traffic": measured_traffic(n)}
-                  for n in rb}
-
-    decode = None
-    if args.decode_steps > 0:
-        decode = time_decode_attention(args, pkv, torch, timing, stream, workloads, np)
+    # each step kernel alone, back to back
+    per_kernel_ms = {"store_indexer_k_fp8": time_back_to_back(torch, timing, stream, store8),
+                     "store_kv_fp4": time_back_to_back(torch, timing, stream, store4),
+                     "gather_indexer_k_fp8": time_back_to_back(torch, timing, stream, gather)}
 
     alg = algorithmic_bytes(T, D, H4, D4, R, maxb)
     step_bytes = sum(alg.values())
-
-    # The NVFP4 store alone, back to back, with the workload's slots and with
-    # the same tokens' slots in page order (same bytes, pages written in
-    # order rather than in the workload's shuffled order).
-    def store_alone(slots):
-        ev = [timing.create(), timing.create()]
-        for _ in range(3):
-            pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slots, k4s, v4s,
-                                 block_size=f.block_size, layout=f.layout)
-        torch.cuda.synchronize()
-        timing.record(ev[0], stream)
-        for _ in range(10):
-            pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slots, k4s, v4s,
-                                 block_size=f.block_size, layout=f.layout)
-        timing.record(ev[1], stream)
-        torch.cuda.synchronize()
-        ms = timing.elapsed_ms(ev[0], ev[1]) / 10
-        timing.destroy_all()
-        return ms
-
-    slot_in_order = torch.arange(T, dtype=torch.int64, device=dev)
-    alone = {"workload_slots": [], "pages_in_order": []}
-    for _ in range(3):  # interleaved, medians reported
-        alone["workload_slots"].append(store_alone(slot4))
-        alone["pages_in_order"].append(store_alone(slot_in_order))
-    store_alone_runs = {}
-    for name, v in alone.items():
-        ms = sorted(v)[len(v) // 2]
-        gbps = alg["store_kv_fp4"] / (ms * 1e-3) / 1e9
-        store_alone_runs[name] = {"us": round(ms * 1e3, 2), "GBps": round(gbps, 1),
-                                  "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
-    store_alone_runs["what"] = ("store_kv_fp4 alone, back-to-back launches (median of three "
-                                "interleaved runs of 10): the workload's slots, and slots 0..T-1 "
-                                "(the same tokens into pages in order)")
-    copy_ceiling = time_d2d_copy(torch, timing, stream, step_bytes)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    kernels = {}
-    for n in names:
-        ms = per_kernel_ms[n]
-        gbps = alg[n] / (ms * 1e-3) / 1e9
-        kernels[n] = {"us": round(ms * 1e3, 2), "alg_bytes": alg[n], "GBps": round(gbps, 1),
-                      "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
-                      "mtokens_per_s": round(T / (ms * 1e-3) / 1e6, 1)}
+    kernels = {n: dict(rate(alg[n], T, per_kernel_ms[n]), traffic=measured_traffic(n))
+               for n in names}
     dom = max(names, key=lambda n: per_kernel_ms[n])
-    dom_gbps = kernels[dom]["GBps"]
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": dom_gbps, "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(dom),
-                "alg_bytes_per_launch": alg[dom]}
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": kernels[dom]["GBps"],
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(kernels[dom]["GBps"] / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic(dom), "alg_bytes_per_launch": alg[dom]}
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     out = {
         "metric": METRIC,
@@ -514,6 +639,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "preroll": {"steps": preroll_steps, "seconds": round(preroll_s, 3),
+                    "what": f"steps launched for a fixed {PREROLL_S} s before the warmup, "
+                            "so that no timed launch meets the clocks' idle state"},
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -529,20 +657,26 @@ def main():
         },
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "mtokens_per_s": round(T / (ms_per_step * 1e-3) / 1e6, 2),
-        "event_ms_per_step": round(sum(per_kernel_ms.values()), 4),
-        "ms_per_step_with_events": round(wall_events * 1e3 / args.steps, 4),
         "kernels": kernels,
+        "kernel_timing": (f"each kernel alone: {B2B_LAUNCHES} launches back to back between "
+                          f"one pair of HIP events, median of {B2B_RUNS} runs"),
         "roofline": roofline,
-        "d2d_copy_same_bytes": copy_ceiling,
-        "store_kv_fp4_alone": store_alone_runs,
         "input_gen_s": round(t_gen, 1),
     }
-    if reader is not None:
-        out["reader_side"] = reader
-    if decode is not None:
-        out["decode_attention"] = decode
+    if not args.no_extras:
+        out["reported"] = time_reported(torch, np, pkv, workloads, timing, stream)
+        reader = time_reader(torch, np, pkv, timing, stream, sets, w, f, bt, cu, c4, k4s, v4s)
+        R4, maxb4 = f.block_table.shape
+        rb = reader_bytes(T, D, H4, D4, R, maxb, R4, maxb4)
+        out["reader_side"] = {n: dict(rate(rb[n], T, reader[n]), traffic=measured_traffic(n))
+                              for n in rb}
+        out["decode_attention"] = time_decode_attention(torch, np, pkv, workloads, timing,
+                                                        stream)
+        del sets
+        torch.cuda.empty_cache()
+        out["d2d_copy_same_bytes"] = time_d2d_copy(torch, timing, stream, step_bytes)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, f, step_bytes)
+        out["cpu_baseline"] = cpu_baseline(w, f)
     print(json.dumps(out), flush=True)
 
 

@@ -45,26 +45,21 @@ CXXFLAGS = [
     "-fno-gpu-flush-denormals-to-zero",
     # no packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # kernel arguments preloaded into SGPRs by the command processor (gfx950
+    # supports it; each code object keeps a fallback that loads them as usual
+    # where the firmware does not): short bandwidth-bound kernels start their
+    # address arithmetic without the kernel-argument round trip (0.3-0.5 us
+    # of an 11-12 us gather).
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-I", INCLUDE,
     "-I", CSRC,
 ]
 
 
-# Per-source additions.  Kernel arguments preloaded into SGPRs by the
-# command processor (gfx950 supports it; the code object keeps a fallback
-# that loads them as usual where the firmware does not): the short
-# bandwidth-bound kernels start their address arithmetic without the
-# kernel-argument round trip (0.3-0.5 us of a 11-12 us gather).
-EXTRA_FLAGS = {
-    "gather_indexer_k_fp8.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-}
-
-
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CXXFLAGS, *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c",
-           os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CXXFLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

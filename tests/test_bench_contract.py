@@ -63,3 +63,28 @@ def test_counter_summary_needs_the_current_kernel_source(tmp_path, monkeypatch):
     path.write_text("traffic_bytes_per_launch: 12345\nsource_sha256: "
                     f"{bench.source_hash('gather_indexer_k_fp8')}\n")
     assert bench.measured_traffic("gather_indexer_k_fp8") == 12345.0
+
+
+def test_cpu_baseline_split_writes_what_one_thread_writes():
+    """The CPU baseline runs the oracle's functions over disjoint token or
+    request ranges on several threads; the bytes they write must be exactly
+    those of one call over everything."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import workloads
+    w = workloads.c4_roundtrip()
+    f = workloads.c5_nvfp4_store(0)
+    one = bench.oracle_ops(w, f, 600)
+    many = bench.oracle_ops(w, f, 600)
+    with ThreadPoolExecutor(3) as pool:
+        for name in ("store_indexer_k_fp8", "store_kv_fp4", "gather_indexer_k_fp8"):
+            fn1, n, *_, out1 = one[name]
+            fn3, _, *_, out3 = many[name]
+            bench.run_split(pool, fn1, n, 1)
+            bench.run_split(pool, fn3, n, 3)
+            for a, b in zip(out1, out3):
+                np.testing.assert_array_equal(a, b)
+    # the ops wrote something: the stores changed their caches, the gather its rows
+    assert (one["store_indexer_k_fp8"][-1][0] != w.cache_init).any()
+    assert (one["store_kv_fp4"][-1][0] != f.cache_init).any()
+    assert (one["gather_indexer_k_fp8"][-1][0] != w.k_fp8_init).any()
