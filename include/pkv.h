@@ -98,7 +98,7 @@ extern "C" {
 #define PKV_DTYPE_F16 1
 
 /* ABI version of this header; bumped when a signature changes. */
-#define PKV_ABI_VERSION 5
+#define PKV_ABI_VERSION 6
 PKV_API int pkv_abi_version(void);
 
 /* Message for the last non-zero status on this thread ("" if none). */
@@ -384,6 +384,38 @@ PKV_API int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_lo
                                        int32_t max_blocks_per_seq, int32_t max_context_len,
                                        int64_t num_blocks, float scale, float k_scale, float v_scale,
                                        int32_t partition_size, void *stream);
+
+/*
+ * Allocation-free variant of pkv_paged_attention_decode, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight
+ * serving loops, harnesses that forbid hipMalloc.  Arguments, results and
+ * errors are those of pkv_paged_attention_decode without its three workspace
+ * buffers: the workspace is carved out of a library-owned device array of
+ * PKV_ATTENTION_SCRATCH_BYTES bytes, one per GPU, held until the process
+ * ends (its address is looked up once per device, on the first call there).
+ * The call allocates nothing.
+ *
+ * A call needs 2 * align256(4 n) + 512 n workspace bytes, n = num_seqs *
+ * num_heads * ceil(max_context_len / partition_size) (head_size 128); one
+ * that needs more than PKV_ATTENTION_SCRATCH_BYTES returns PKV_EUNSUPPORTED
+ * and enqueues nothing (PKV_ELAUNCH if the array's address cannot be looked
+ * up).  Every workspace element a call reads was written earlier in the
+ * same call, so nothing carries over from one call to the next.  All calls
+ * on one GPU share its array: calls that may run at the same time on one
+ * GPU (on different streams, or enqueued from different threads without
+ * ordering) race and give undefined results; order them on one stream.
+ */
+#define PKV_ATTENTION_SCRATCH_BYTES (32u << 20)
+PKV_API int pkv_paged_attention_decode_noalloc(void *out, const void *query,
+                                               const void *key_cache, const void *value_cache,
+                                               const int32_t *block_tables,
+                                               const int32_t *context_lens, int32_t num_seqs,
+                                               int32_t num_heads, int32_t num_kv_heads,
+                                               int32_t head_size, int32_t block_size,
+                                               int32_t max_blocks_per_seq,
+                                               int32_t max_context_len, int64_t num_blocks,
+                                               float scale, float k_scale, float v_scale,
+                                               int32_t partition_size, void *stream);
 
 /* Host-only query (no GPU work): the number of work units the balanced split
  * of pkv_paged_attention_decode uses for these sizes when the device holds

@@ -20,6 +20,7 @@ __all__ = [
     "pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
     "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant", "pkv_fp8_mqa_logits",
     "pkv_paged_attention_decode", "paged_attention_workspace", "pkv_attention_balanced_units",
+    "pkv_paged_attention_decode_noalloc", "ATTENTION_SCRATCH_BYTES",
     "pkv_diag_narrow",
     "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "PkvError", "LAYOUT_HND", "LAYOUT_NHD",
     "library_path", "abi_version",
@@ -30,6 +31,7 @@ LAYOUT_NHD = 1
 DTYPE_BF16 = 0
 DTYPE_F16 = 1
 SCALE_BYTES = 4
+ATTENTION_SCRATCH_BYTES = 32 << 20   # PKV_ATTENTION_SCRATCH_BYTES
 
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkv.so")
 
@@ -85,12 +87,15 @@ def _load():
     f32 = ctypes.c_float
     lib.pkv_paged_attention_decode.argtypes = [P, P, P, P, P, P, P, P, P, i32, i32, i32, i32, i32,
                                                i32, i32, i64, f32, f32, f32, i32, P]
+    lib.pkv_paged_attention_decode_noalloc.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32,
+                                                       i32, i32, i32, i64, f32, f32, f32, i32, P]
     lib.pkv_attention_balanced_units.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.pkv_attention_balanced_units.restype = i64
     for name in ("pkv_gather_indexer_k_fp8", "pkv_store_indexer_k_fp8", "pkv_store_kv_fp4",
                  "pkv_gather_indexer_k_dequant", "pkv_gather_kv_fp4_dequant",
                  "pkv_diag_encode_e4m3", "pkv_diag_encode_e2m1", "pkv_diag_narrow",
-                 "pkv_fp8_mqa_logits", "pkv_paged_attention_decode"):
+                 "pkv_fp8_mqa_logits", "pkv_paged_attention_decode",
+                 "pkv_paged_attention_decode_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -441,6 +446,41 @@ def paged_attention_workspace(num_seqs: int, num_heads: int, max_context_len: in
     return exp_sums, max_logits, tmp_out
 
 
+def _attention_shapes(out, query, key_cache, value_cache, num_kv_heads, block_tables,
+                      context_lens, block_size):
+    """Checks the decode-attention tensors; returns (num_seqs, num_heads,
+    head_size, num_blocks)."""
+    _dev(out, "out", torch.bfloat16)
+    _dev(query, "query", torch.bfloat16)
+    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
+        _dev(t, n)
+        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{n} must be uint8 or float8_e4m3fn")
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32)
+    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
+                 (value_cache, "value_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens")):
+        _contig(t, n)
+    if query.dim() != 3:
+        raise ValueError("query must be [num_seqs, num_heads, head_size]")
+    num_seqs, num_heads, head_size = query.shape
+    if tuple(out.shape) != tuple(query.shape):
+        raise ValueError("out must have the shape of query")
+    if key_cache.dim() != 5 or value_cache.dim() != 4:
+        raise ValueError("key_cache must be [nb, KVH, D/16, B, 16] and value_cache [nb, KVH, D, B]")
+    num_blocks = key_cache.shape[0]
+    if (tuple(key_cache.shape) != (num_blocks, num_kv_heads, head_size // 16, block_size, 16) or
+            tuple(value_cache.shape) != (num_blocks, num_kv_heads, head_size, block_size)):
+        raise ValueError("key_cache / value_cache shapes do not match num_kv_heads, head_size "
+                         "and block_size")
+    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
+        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
+    if context_lens.numel() != num_seqs:
+        raise ValueError("context_lens must have num_seqs entries")
+    return num_seqs, num_heads, head_size, num_blocks
+
+
 def pkv_paged_attention_decode(out, exp_sums, max_logits, tmp_out, query, key_cache,
                                value_cache, num_kv_heads: int, scale: float, block_tables,
                                context_lens, block_size: int, max_context_len: int,
@@ -459,37 +499,11 @@ def pkv_paged_attention_decode(out, exp_sums, max_logits, tmp_out, query, key_ca
     block_tables: int32 [num_seqs, max_blocks_per_seq]; context_lens int32 [num_seqs].
     scale, k_scale, v_scale: host floats.
     """
-    _dev(out, "out", torch.bfloat16)
-    _dev(query, "query", torch.bfloat16)
-    for t, n in ((key_cache, "key_cache"), (value_cache, "value_cache")):
-        _dev(t, n)
-        if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
-            raise TypeError(f"{n} must be uint8 or float8_e4m3fn")
+    num_seqs, num_heads, head_size, num_blocks = _attention_shapes(
+        out, query, key_cache, value_cache, num_kv_heads, block_tables, context_lens, block_size)
     for t, n in ((exp_sums, "exp_sums"), (max_logits, "max_logits"), (tmp_out, "tmp_out")):
         _dev(t, n, torch.float32)
-    _dev(block_tables, "block_tables", torch.int32)
-    _dev(context_lens, "context_lens", torch.int32)
-    for t, n in ((out, "out"), (query, "query"), (key_cache, "key_cache"),
-                 (value_cache, "value_cache"), (exp_sums, "exp_sums"),
-                 (max_logits, "max_logits"), (tmp_out, "tmp_out"),
-                 (block_tables, "block_tables"), (context_lens, "context_lens")):
         _contig(t, n)
-    if query.dim() != 3:
-        raise ValueError("query must be [num_seqs, num_heads, head_size]")
-    num_seqs, num_heads, head_size = query.shape
-    if tuple(out.shape) != tuple(query.shape):
-        raise ValueError("out must have the shape of query")
-    if key_cache.dim() != 5 or value_cache.dim() != 4:
-        raise ValueError("key_cache must be [nb, KVH, D/16, B, 16] and value_cache [nb, KVH, D, B]")
-    num_blocks = key_cache.shape[0]
-    if (tuple(key_cache.shape) != (num_blocks, num_kv_heads, head_size // 16, block_size, 16) or
-            tuple(value_cache.shape) != (num_blocks, num_kv_heads, head_size, block_size)):
-        raise ValueError("key_cache / value_cache shapes do not match num_kv_heads, head_size "
-                         "and block_size")
-    if block_tables.dim() != 2 or block_tables.shape[0] != num_seqs:
-        raise ValueError("block_tables must be [num_seqs, max_blocks_per_seq]")
-    if context_lens.numel() != num_seqs:
-        raise ValueError("context_lens must have num_seqs entries")
     parts = -(-int(max_context_len) // int(partition_size)) if partition_size > 0 else 0
     if exp_sums.dim() != 3 or tuple(exp_sums.shape[:2]) != (num_seqs, num_heads) or \
             tuple(max_logits.shape) != tuple(exp_sums.shape) or \
@@ -503,6 +517,24 @@ def pkv_paged_attention_decode(out, exp_sums, max_logits, tmp_out, query, key_ca
         context_lens.data_ptr(), num_seqs, num_heads, num_kv_heads, head_size, block_size,
         block_tables.shape[1], max_context_len, num_blocks, scale, k_scale, v_scale,
         partition_size, _stream(stream)))
+
+
+def pkv_paged_attention_decode_noalloc(out, query, key_cache, value_cache, num_kv_heads: int,
+                                       scale: float, block_tables, context_lens,
+                                       block_size: int, max_context_len: int,
+                                       k_scale: float = 1.0, v_scale: float = 1.0,
+                                       partition_size: int = 256, stream=None):
+    """pkv_paged_attention_decode with the library's built-in workspace (no
+    allocation by the call, ATTENTION_SCRATCH_BYTES per GPU, shared by every
+    call on that GPU: calls that may overlap on one GPU race).  Arguments as
+    there, without the three workspace tensors."""
+    num_seqs, num_heads, head_size, num_blocks = _attention_shapes(
+        out, query, key_cache, value_cache, num_kv_heads, block_tables, context_lens, block_size)
+    _check(_lib.pkv_paged_attention_decode_noalloc(
+        out.data_ptr(), query.data_ptr(), key_cache.data_ptr(), value_cache.data_ptr(),
+        block_tables.data_ptr(), context_lens.data_ptr(), num_seqs, num_heads, num_kv_heads,
+        head_size, block_size, block_tables.shape[1], max_context_len, num_blocks, scale,
+        k_scale, v_scale, partition_size, _stream(stream)))
 
 
 def pkv_attention_balanced_units(num_seqs: int, num_heads: int, num_kv_heads: int,

@@ -314,15 +314,18 @@ int pkv_fp8_mqa_logits(const void* q, int64_t q_token_stride, const void* k, con
   return launched(pkv::launch_fp8_mqa_logits(a, static_cast<hipStream_t>(stream)), op);
 }
 
-int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, float* tmp_out,
-                               const void* query, const void* key_cache, const void* value_cache,
-                               const int32_t* block_tables, const int32_t* context_lens,
-                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
-                               int32_t max_context_len, int64_t num_blocks, float scale,
-                               float k_scale, float v_scale, int32_t partition_size,
-                               void* stream) {
-  static const char* op = "pkv_paged_attention_decode";
+}  // extern "C"
+
+namespace {
+
+// Checks shared by both decode-attention entry points (everything but the
+// workspace buffers).
+int check_attention(const char* op, const void* out, const void* query, const void* key_cache,
+                    const void* value_cache, const int32_t* block_tables,
+                    const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                    int32_t num_kv_heads, int32_t head_size, int32_t block_size,
+                    int32_t max_blocks_per_seq, int32_t max_context_len, int64_t num_blocks,
+                    float scale, float k_scale, float v_scale, int32_t partition_size) {
   if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs must be >= 0, got %d", op, num_seqs);
   if (num_heads <= 0 || num_kv_heads <= 0)
     return fail(PKV_EINVAL, "%s: num_heads and num_kv_heads must be > 0, got %d and %d", op,
@@ -354,17 +357,86 @@ int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, fl
     return fail(PKV_EUNSUPPORTED, "%s: num_seqs * num_heads and the partition count must stay below 2^31", op);
   if ((int64_t)num_seqs * max_blocks_per_seq > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "%s: num_seqs * max_blocks_per_seq exceeds 2^31-1", op);
-  if (num_seqs == 0) return ok();
-  if (!out || !query || !context_lens || (max_context_len > 0 &&
-      (!exp_sums || !max_logits || !tmp_out || !key_cache || !value_cache || !block_tables)))
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !query || !context_lens ||
+      (max_context_len > 0 && (!key_cache || !value_cache || !block_tables)))
     return fail(PKV_EINVAL, "%s: null buffer pointer", op);
-  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(tmp_out, 16) || !aligned(key_cache, 16) ||
-      !aligned(value_cache, 16))
-    return fail(PKV_EALIGN, "%s: out, query, tmp_out, key_cache and value_cache must be 16-byte aligned", op);
-  if (!aligned(exp_sums, 4) || !aligned(max_logits, 4) || !aligned(block_tables, 4) ||
-      !aligned(context_lens, 4))
-    return fail(PKV_EALIGN, "%s: exp_sums, max_logits, block_tables and context_lens must be 4-byte aligned", op);
+  if (!aligned(out, 16) || !aligned(query, 16) || !aligned(key_cache, 16) || !aligned(value_cache, 16))
+    return fail(PKV_EALIGN, "%s: out, query, key_cache and value_cache must be 16-byte aligned", op);
+  if (!aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PKV_EALIGN, "%s: block_tables and context_lens must be 4-byte aligned", op);
+  return PKV_OK;
+}
+
+int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_decode(void* out, float* exp_sums, float* max_logits, float* tmp_out,
+                               const void* query, const void* key_cache, const void* value_cache,
+                               const int32_t* block_tables, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_size, int32_t block_size, int32_t max_blocks_per_seq,
+                               int32_t max_context_len, int64_t num_blocks, float scale,
+                               float k_scale, float v_scale, int32_t partition_size,
+                               void* stream) {
+  static const char* op = "pkv_paged_attention_decode";
+  if (int rc = check_attention(op, out, query, key_cache, value_cache, block_tables, context_lens,
+                               num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                               max_blocks_per_seq, max_context_len, num_blocks, scale, k_scale,
+                               v_scale, partition_size))
+    return rc;
+  if (num_seqs == 0) return ok();
+  if (max_context_len > 0 && (!exp_sums || !max_logits || !tmp_out))
+    return fail(PKV_EINVAL, "%s: null buffer pointer", op);
+  if (!aligned(tmp_out, 16))
+    return fail(PKV_EALIGN, "%s: tmp_out must be 16-byte aligned", op);
+  if (!aligned(exp_sums, 4) || !aligned(max_logits, 4))
+    return fail(PKV_EALIGN, "%s: exp_sums and max_logits must be 4-byte aligned", op);
   pkv::PagedAttentionArgs a{static_cast<uint16_t*>(out), exp_sums, max_logits, tmp_out,
+                            static_cast<const uint16_t*>(query),
+                            static_cast<const uint8_t*>(key_cache),
+                            static_cast<const uint8_t*>(value_cache), block_tables, context_lens,
+                            num_seqs, num_heads, num_kv_heads, block_size, max_blocks_per_seq,
+                            max_context_len, num_blocks, scale, k_scale, v_scale, partition_size};
+  return launched(pkv::launch_paged_attention_decode(a, static_cast<hipStream_t>(stream)), op);
+}
+
+int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void* key_cache,
+                                       const void* value_cache, const int32_t* block_tables,
+                                       const int32_t* context_lens, int32_t num_seqs,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_size,
+                                       int32_t block_size, int32_t max_blocks_per_seq,
+                                       int32_t max_context_len, int64_t num_blocks, float scale,
+                                       float k_scale, float v_scale, int32_t partition_size,
+                                       void* stream) {
+  static const char* op = "pkv_paged_attention_decode_noalloc";
+  if (int rc = check_attention(op, out, query, key_cache, value_cache, block_tables, context_lens,
+                               num_seqs, num_heads, num_kv_heads, head_size, block_size,
+                               max_blocks_per_seq, max_context_len, num_blocks, scale, k_scale,
+                               v_scale, partition_size))
+    return rc;
+  if (num_seqs == 0) return ok();
+  // workspace [exp_sums | max_logits | tmp_out] as pkv_paged_attention_decode's,
+  // each region 256-byte aligned
+  const int64_t parts = ((int64_t)max_context_len + partition_size - 1) / partition_size;
+  const int64_t n = (int64_t)num_seqs * num_heads * (parts > 0 ? parts : 1);
+  const int64_t sums = align256(4 * n);
+  const int64_t need = 2 * sums + 4 * n * head_size;
+  if (need > (int64_t)PKV_ATTENTION_SCRATCH_BYTES)
+    return fail(PKV_EUNSUPPORTED,
+                "%s: the call needs %lld bytes of workspace, more than the %lld-byte built-in "
+                "scratch (use pkv_paged_attention_decode with a caller workspace)",
+                op, (long long)need, (long long)PKV_ATTENTION_SCRATCH_BYTES);
+  void* base = nullptr;
+  if (int e = pkv::attention_scratch(&base))
+    return fail(PKV_ELAUNCH, "%s: looking up the scratch array failed: %s", op,
+                hipGetErrorString(static_cast<hipError_t>(e)));
+  uint8_t* b = static_cast<uint8_t*>(base);
+  pkv::PagedAttentionArgs a{static_cast<uint16_t*>(out), reinterpret_cast<float*>(b),
+                            reinterpret_cast<float*>(b + sums), reinterpret_cast<float*>(b + 2 * sums),
                             static_cast<const uint16_t*>(query),
                             static_cast<const uint8_t*>(key_cache),
                             static_cast<const uint8_t*>(value_cache), block_tables, context_lens,

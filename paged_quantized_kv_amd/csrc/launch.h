@@ -152,6 +152,8 @@ int launch_fp8_mqa_logits(const MqaLogitsArgs& a, hipStream_t stream);
 int launch_gather_indexer_k_dequant(const GatherDequantArgs& a, hipStream_t stream);
 int launch_gather_kv_fp4_dequant(const GatherFp4DequantArgs& a, hipStream_t stream);
 int launch_paged_attention_decode(const PagedAttentionArgs& a, hipStream_t stream);
+// Device address of the current GPU's attention scratch array (0 or a HIP error).
+int attention_scratch(void** ptr);
 // Units of the decode attention's balanced split for these sizes (0: fixed split).
 int64_t attention_balanced_units(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t max_context_len, int32_t partition_size,

@@ -729,6 +729,12 @@ __global__ __launch_bounds__(kPaThreads) void paged_attention_reduce_kernel(
   dst[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
 }
 
+// Workspace of the allocation-free entry point: one array per GPU, loaded
+// with the code object and held until the process ends.  Host code never
+// uses its name as an address (on the host it is only a stand-in); the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[PKV_ATTENTION_SCRATCH_BYTES];
+
 // Wave slots of the device for the partition kernels (three waves per SIMD,
 // four SIMDs per compute unit), cached per device (threads that race on the
 // first call store the same value).
@@ -749,6 +755,26 @@ int partition_wave_slots() {
 }
 
 }  // namespace
+
+// Device address of this GPU's scratch array (the current device's), looked
+// up on the first call on each device and cached; threads that race on the
+// first call store the same value.  Returns 0 or a HIP error code.
+int attention_scratch(void** ptr) {
+  static std::atomic<void*> per_device[64];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+  void* p = per_device[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (p == nullptr) return (int)hipErrorInvalidSymbol;
+    per_device[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return 0;
+}
 
 // Units of the balanced split, or 0 for the fixed split: the balanced one
 // needs more than one partition of workspace per sequence, at most 64 * 64

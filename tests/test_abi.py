@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
     for s in declared_symbols():
         assert s in exported, s
         assert getattr(lib, s) is not None
-    assert pkv.abi_version() == 5
+    assert pkv.abi_version() == 6
     # nothing else of the library is exported (the compiler's own
     # per-translation-unit ids aside)
     others = [name for name in re.findall(r"^\S*\s*\S+ (\S+)$", out, re.M)
@@ -287,6 +287,39 @@ def test_paged_attention_validation(kw, code, msg):
 
 def test_paged_attention_empty_is_ok():
     assert pa(S=0, out=0, es=0, ml=0, tmp=0, q=0, kc=0, vc=0, bt=0, cl=0) == PKV_OK
+
+
+def pan(**kw):
+    a = dict(out=A, q=A, kc=A, vc=A, bt=A, cl=A, S=4, H=64, KVH=8, D=128, B=16, maxb=8,
+             maxc=128, nb=64, scale=0.088, ksc=0.03, vsc=0.04, P=256)
+    a.update(kw)
+    return lib().pkv_paged_attention_decode_noalloc(a["out"], a["q"], a["kc"], a["vc"], a["bt"],
+                                                    a["cl"], a["S"], a["H"], a["KVH"], a["D"],
+                                                    a["B"], a["maxb"], a["maxc"], a["nb"],
+                                                    a["scale"], a["ksc"], a["vsc"], a["P"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(S=-1), PKV_EINVAL, "num_seqs"),
+    (dict(H=60), PKV_EINVAL, "not a multiple"),
+    (dict(P=384), PKV_EUNSUPPORTED, "partition_size"),
+    (dict(out=0), PKV_EINVAL, "null"),
+    (dict(kc=A + 8), PKV_EALIGN, "16-byte"),
+    # 4096 x 64 heads x 64 partitions: 2 x 4 MiB + 2 GiB of workspace, over the 32 MiB
+    (dict(S=4096, maxb=4096, maxc=65536, P=1024), PKV_EUNSUPPORTED, "built-in scratch"),
+    # just over: n = 1009 * 64 gives 2 * align256(4 n) + 512 n = 33579520 > 2^25
+    # (1008 sequences, 33546240 bytes, would fit)
+    (dict(S=1009, H=64, KVH=8, maxc=256, P=256), PKV_EUNSUPPORTED, "built-in scratch"),
+])
+def test_paged_attention_noalloc_validation(kw, code, msg):
+    """Every check runs on the host before any HIP call, so none of these
+    reaches the device."""
+    assert pan(**kw) == code
+    assert msg in last_error()
+
+
+def test_paged_attention_noalloc_empty_is_ok():
+    assert pan(S=0, out=0, q=0, kc=0, vc=0, bt=0, cl=0) == PKV_OK
 
 
 def test_diag_validation():
