@@ -79,6 +79,30 @@ __device__ __forceinline__ v4f mfma_bf16(const v8bf a, const v8bf b, const v4f c
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// An MFMA, then a gap: nothing is scheduled across the two barriers,
+// and the s_nop between them is 8 wait states, so no later instruction can
+// rewrite the MFMA's source or accumulator registers, or read its result,
+// sooner than 8 wait states after it issued.  Without the gap the compiler
+// lets a key conversion overwrite the chain's previous accumulator register
+// 3 wait states after the MFMA that reads it as SrcC (the logits chains
+// alternate dst and SrcC between two register quads), the closest its hazard
+// model allows for this 4-pass instruction; a build whose K steps were
+// interleaved across tiles had the same pattern and gave wrong results that
+// depended on timing.  8 wait states is more than twice that distance.  The
+// P.V pairs (high then low probability half into one output) alternate the
+// same way; there the register the first MFMA frees is the second one's
+// destination, so one gap after the pair suffices.
+__device__ __forceinline__ void mfma_gap() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ v4f mfma_bf16_gap(const v8bf a, const v8bf b, const v4f c) {
+  const v4f d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  mfma_gap();
+  return d;
+}
+
 // 8 E4M3 codes (little-endian in two dwords) -> 8 bf16, exact: the gfx950
 // scaled converter with unit scale, two codes per instruction (every E4M3
 // value has at most 4 significant bits and lies in bf16's range).
@@ -332,11 +356,11 @@ __device__ __forceinline__ void attend_segment(
     auto tile_logits = [&](auto mc) {
       constexpr int m = decltype(mc)::value;
       const u32x4 w0 = key_operand<m, 0>(kw);
-      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w0.x, w0.y}), bq[0], acc[m]);
-      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w0.z, w0.w}), bq[1], acc[m]);
+      acc[m] = mfma_bf16_gap(fp8x8_to_bf16(u32x2{w0.x, w0.y}), bq[0], acc[m]);
+      acc[m] = mfma_bf16_gap(fp8x8_to_bf16(u32x2{w0.z, w0.w}), bq[1], acc[m]);
       const u32x4 w1 = key_operand<m, 1>(kw);
-      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w1.x, w1.y}), bq[2], acc[m]);
-      acc[m] = mfma_bf16(fp8x8_to_bf16(u32x2{w1.z, w1.w}), bq[3], acc[m]);
+      acc[m] = mfma_bf16_gap(fp8x8_to_bf16(u32x2{w1.x, w1.y}), bq[2], acc[m]);
+      acc[m] = mfma_bf16_gap(fp8x8_to_bf16(u32x2{w1.z, w1.w}), bq[3], acc[m]);
     };
     tile_logits(std::integral_constant<int, 0>{});
     tile_logits(std::integral_constant<int, 1>{});
@@ -419,6 +443,7 @@ __device__ __forceinline__ void attend_segment(
         const v8bf a = fp8x8_to_bf16(sp2 ? u32x2{w.z, w.w} : u32x2{w.x, w.y});
         o[n] = mfma_bf16(a, bhi, o[n]);
         o[n] = mfma_bf16(a, blo, o[n]);
+        mfma_gap();
       }
     }
     if constexpr (kPrefetch) {
