@@ -121,8 +121,8 @@ def parse_args():
     p.add_argument("--no-extras", action="store_true",
                    help="time only the step and its three kernels (short profiling runs)")
     p.add_argument("--calibration-copy", action="store_true",
-                   help="run a plain 256 MiB fp32 copy-like kernel (torch.neg) before the "
-                        "timed steps, for scaling hardware byte counters")
+                   help="run a plain fp32 copy-like kernel (torch.neg) over 16 MiB to 1 GiB "
+                        "before the timed steps, for scaling hardware byte counters")
     return p.parse_args()
 
 
@@ -605,12 +605,15 @@ def main():
     timing = HipTimingEvents(lead=lead)
 
     if args.calibration_copy:
-        src = torch.randn(64 << 20, device=dev)          # 256 MiB fp32
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.neg(src, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        # 16 MiB, 64 MiB, 256 MiB and 1 GiB of fp32 each way, three times each:
+        # the counters' scale factors at several sizes
+        for mib in (16, 64, 256, 1024):
+            src = torch.randn(mib << 18, device=dev)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                torch.neg(src, out=dst)
+            torch.cuda.synchronize()
+            del src, dst
 
     # fixed pre-roll: steps for PREROLL_S of wall clock, in batches of 20
     t_pre = time.perf_counter()
