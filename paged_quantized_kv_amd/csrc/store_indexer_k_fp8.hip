@@ -45,25 +45,35 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wave_id = ((int64_t)blockIdx.x * kStoreThreads + threadIdx.x) / kWave;
   const int part = lane % kLanes;
+  const int64_t last_token = num_tokens - 1;
+  const int last_chunk = head_dim / 8 - 1;
 
-  // ---- issue the loads of every token group first
+  // ---- every group's loads, unconditional (rows past the end re-read the
+  // last row, chunks past head_dim the last chunk; neither is stored)
   u32x4 xv[kStoreUnroll][kChunks];
   int64_t slot[kStoreUnroll];
 #pragma unroll
   for (int u = 0; u < kStoreUnroll; ++u) {
     const int64_t t = (wave_id * kStoreUnroll + u) * kTokensPerWave + lane / kLanes;
-    slot[u] = -1;
+    const int64_t tc = t < num_tokens ? t : last_token;
+    slot[u] = slot_mapping[tc];
+    if (t >= num_tokens) slot[u] = -1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + tc * k_row_stride);
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) xv[u][c] = u32x4{0u, 0u, 0u, 0u};
-    if (t < num_tokens) {
-      slot[u] = slot_mapping[t];
-      const u32x4* src = reinterpret_cast<const u32x4*>(k + t * k_row_stride);
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c)
-        if ((part + c * kLanes) * 8 < head_dim) xv[u][c] = load_stream(src + part + c * kLanes);
+    for (int c = 0; c < kChunks; ++c) {
+      const int ch = part + c * kLanes;
+      xv[u][c] = load_stream(src + (ch < last_chunk ? ch : last_chunk));
     }
   }
 
+  // ---- quantize group by group (each waits only for its own loads); the
+  // stores follow once every group is done, so no store is outstanding while
+  // a later group's loads are awaited
+  u32x2 codes[kStoreUnroll][kChunks];
+  float sv[kStoreUnroll];
+  uint8_t* base[kStoreUnroll];
+  int64_t offv[kStoreUnroll];
+  bool keep[kStoreUnroll];
 #pragma unroll
   for (int u = 0; u < kStoreUnroll; ++u) {
     float x[kChunks][8];
@@ -71,24 +81,23 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
       unpack8_src<kF16>(xv[u][c], x[c]);
+      const bool in = (part + c * kLanes) * 8 < head_dim;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, abs_bits(x[c][i]));
+      for (int i = 0; i < 8; ++i) m = max(m, in ? abs_bits(x[c][i]) : 0u);
     }
     m = group_max<kLanes>(m);  // all 64 lanes take part
-    if (slot[u] < 0) continue;
-    int64_t page, off;
-    split_slot(slot[u], block_size, log2_bs, page, off);
-    if (page >= num_blocks) continue;
-
+    int64_t page = 0, off = 0;
+    if (slot[u] >= 0) split_slot(slot[u], block_size, log2_bs, page, off);
+    keep[u] = slot[u] >= 0 && page < num_blocks;
     const float amax = __uint_as_float(m);
     const bool fast = amax >= 0x1p-60f;
     const float s = amax / 448.0f;
     const float rs = fast ? 1.0f / s : 0.0f;
-    uint8_t* page_base = kv_cache + page * page_stride;
+    sv[u] = s;
+    base[u] = kv_cache + page * page_stride;
+    offv[u] = off;
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
-      const int e0 = (part + c * kLanes) * 8;
-      if (e0 >= head_dim) continue;
       float y[8];
       if (fast) {
 #pragma unroll
@@ -97,13 +106,21 @@ __global__ __launch_bounds__(kStoreThreads) void store_indexer_k_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) y[i] = (s == 0.0f) ? x[c][i] : x[c][i] / s;
       }
-      u32x2 codes;
-      codes.x = e4m3_pack4(y[0], y[1], y[2], y[3]);
-      codes.y = e4m3_pack4(y[4], y[5], y[6], y[7]);
-      *reinterpret_cast<u32x2*>(page_base + off * head_dim + e0) = codes;
+      codes[u][c].x = e4m3_pack4(y[0], y[1], y[2], y[3]);
+      codes[u][c].y = e4m3_pack4(y[4], y[5], y[6], y[7]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kStoreUnroll; ++u) {
+    if (!keep[u]) continue;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int e0 = (part + c * kLanes) * 8;
+      if (e0 < head_dim)
+        *reinterpret_cast<u32x2*>(base[u] + offv[u] * head_dim + e0) = codes[u][c];
     }
     if (part == 0)
-      *reinterpret_cast<float*>(page_base + (int64_t)block_size * head_dim + off * 4) = s;
+      *reinterpret_cast<float*>(base[u] + (int64_t)block_size * head_dim + offv[u] * 4) = sv[u];
   }
 }
 
