@@ -16,6 +16,21 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long CPU sweep")
 
 
+GPU_TEST_TIMEOUT_S = 300  # the longest GPU test takes well under a minute
+
+
+def pytest_collection_modifyitems(config, items):
+    """Every GPU test without a timeout of its own gets one (when the
+    pytest-timeout plugin is there), enforced from a watchdog thread, which
+    can end a test that is waiting inside a GPU call: a run without
+    --timeout then still ends, naming the test, instead of waiting forever."""
+    if not config.pluginmanager.hasplugin("timeout"):
+        return
+    for item in items:
+        if item.get_closest_marker("gpu") and not item.get_closest_marker("timeout"):
+            item.add_marker(pytest.mark.timeout(GPU_TEST_TIMEOUT_S, method="thread"))
+
+
 def load_golden(name):
     with open(os.path.join(GOLDEN, name)) as f:
         return json.load(f)
