@@ -36,8 +36,9 @@ Timing, in this order:
     the host between the events;
     `roofline` describes the kernel with the longest duration;
   - reported workloads (not part of `value`): the gather on 8 long ragged
-    requests, the 16 x 512-token store-then-gather round trip and the NVFP4
-    store of [4096, 8, 128] K and V, each timed the same way;
+    requests, the 16 x 512-token store-then-gather round trip, the NVFP4
+    store of [4096, 8, 128] K and V, and the step's NVFP4 store with its
+    tokens stored to pages in order, each timed the same way;
   - the reader side (pkv_gather_indexer_k_dequant, pkv_gather_kv_fp4_dequant)
     on the prefill batch and the decode consumer (pkv_paged_attention_decode,
     200 requests with Llama-3.1-70B attention shapes) on its own batch, timed
@@ -185,13 +186,13 @@ class HipTimingEvents:
             self._hip.hipEventDestroy(ev)
 
 
-def time_back_to_back(torch, timing, stream, launch, n=B2B_LAUNCHES, runs=B2B_RUNS):
+def time_back_to_back(torch, timing, stream, launch, n=B2B_LAUNCHES, runs=B2B_RUNS, warm=4):
     """Median over `runs` of the average duration (ms) of `n` launches issued
     back to back between one pair of events on the launch stream; launch(i)
     enqueues the i-th launch.  Each run starts behind timing.lead (when set),
     so the GPU never waits for the host between the two events."""
     e0, e1 = timing.create(), timing.create()
-    for i in range(4):
+    for i in range(warm):
         launch(i)
     torch.cuda.synchronize()
     avgs = []
@@ -694,6 +695,25 @@ def main():
                               for n in rb}
         out["decode_attention"] = time_decode_attention(torch, np, pkv, workloads, timing,
                                                         stream)
+        # the step's NVFP4 store with the same tokens stored to pages in order
+        # (slot = token index): the kernel when the placement of the pages does
+        # not scatter its writes (after the reader side, which reads the pages
+        # the workload's slots wrote)
+        assert c4.shape[0] * f.block_size >= T
+        slot_in_order = torch.arange(T, dtype=torch.int64, device=dev)
+
+        def store4_in_order(i):
+            pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], slot_in_order, k4s, v4s,
+                                 block_size=f.block_size, layout=f.layout)
+
+        # 64 untimed launches first: after the stores into shuffled pages the
+        # in-order store takes about 40 launches to settle (trace: 245-288 us
+        # at first, then 212-218 us)
+        ms = time_back_to_back(torch, timing, stream, store4_in_order, warm=64)
+        out["reported"]["nvfp4_store_256x1000_pages_in_order"] = dict(
+            rate(alg["store_kv_fp4"], T, ms),
+            workload="the step's NVFP4 store (256 x 1000 tokens, H=8, D=128, B=16, HND) with "
+                     "slot = token index instead of the workload's shuffled pages")
         del sets
         torch.cuda.empty_cache()
         out["d2d_copy_same_bytes"] = time_d2d_copy(torch, timing, stream, step_bytes)
