@@ -259,3 +259,36 @@ def test_model_catches_planted_mistakes(mistake):
         assert np.all(writes[:, :cols][valid] == 1) and np.all(writes[:, :cols][~valid] == 0)
         assert np.allclose(out[:, :cols][valid], ref[valid], rtol=1e-12,
                            atol=1e-12 * np.abs(ref[valid]).max())
+
+
+def test_model_on_the_gathered_keys_case():
+    """The GPU case on keys the path produced: the fp8 store of bf16 K, then
+    the gather back; 16 requests of 512 tokens with causal ranges."""
+    w = workloads.c4_roundtrip()
+    cache = w.cache_init.copy()
+    oracle.store_indexer_k_fp8(w.k_bits, w.slot_mapping, cache, w.block_size, w.head_dim)
+    T = int(w.cu_seq_lens[-1])
+    kf = np.zeros((T, 128), np.uint8)
+    ksb = np.zeros((T, 4), np.uint8)
+    oracle.gather_indexer_k_fp8(cache, kf, ksb, w.block_table, w.cu_seq_lens, w.block_size, 128)
+    k_scale = ksb.view(np.float32).reshape(T)
+    keep = w.slot_mapping[:T] >= 0
+    g = workloads.mqa_logits_case(11, num_q=0, num_heads=64, num_k=0,
+                                  causal_lens=list(np.diff(w.cu_seq_lens)))
+    kf[~keep] = 0
+    k_scale = np.where(keep, k_scale, 0).astype(np.float32)
+    # the first request (512 query tokens) keeps the model's run short
+    n = 512
+    check_case(np.ascontiguousarray(g.q[:n]), kf, k_scale, np.ascontiguousarray(g.weights[:n]),
+               np.ascontiguousarray(g.ks[:n]), np.ascontiguousarray(g.ke[:n]), 512)
+
+
+def test_model_on_the_extreme_codes_case():
+    g = workloads.mqa_logits_case(13, num_q=16, num_heads=64, num_k=80)
+    q, k = g.q.copy(), g.k.copy()
+    q[0] = 0x7E
+    q[1] = 0xFE
+    k[:8] = 0x7E
+    k[8:16] = 0x01
+    q[2, :, ::8] = 0x7E
+    check_case(q, k, g.k_scale, g.weights, g.ks, g.ke, 80)
