@@ -345,15 +345,12 @@ int launch_prefix(const GatherArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-#ifndef PKV_GATHER_MODE
-#define PKV_GATHER_MODE 0  // 0: choose per call, 1: always prefix scan, 2: always direct
-#endif
 
 int launch_gather_indexer_k_fp8(const GatherArgs& a, hipStream_t stream) {
   // Upper bound on page runs when the rows fit num_tokens: sum(len)/B + R.
   const int64_t table = (int64_t)a.num_reqs * a.max_blocks_per_req;
   const int64_t run_bound = (a.num_tokens + a.block_size - 1) / a.block_size + a.num_reqs;
-  const bool direct = PKV_GATHER_MODE == 2 || (PKV_GATHER_MODE == 0 && table <= 2 * run_bound);
+  const bool direct = table <= 2 * run_bound;
   if (!direct) return launch_prefix(a, stream);
   // kK * kU = 16 chunks per lane in flight (8 runs per wave at most).
   switch (fast_chunks_per_lane(a.block_size, a.head_dim)) {

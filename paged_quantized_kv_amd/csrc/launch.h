@@ -10,14 +10,12 @@ namespace pkv {
 
 // One workgroup stages cu_seq_lens and the run prefix of up to this many
 // requests in LDS (4 bytes each, under 64 KiB with the static scratch);
-// larger tables are launched in
-// request chunks.
+// larger tables are launched in request chunks.
 constexpr int64_t kGatherMaxReqsPerLaunch = 16000;
+// Grid caps of the grid-stride kernels (the gather's prefix kernel, the
+// read-backs, the NVFP4 store): larger inputs loop.
 constexpr int64_t kGatherMaxBlocks = 65536;
-#ifndef PKV_FP4_MAX_BLOCKS
-#define PKV_FP4_MAX_BLOCKS 65536
-#endif
-constexpr int64_t kFp4MaxBlocks = PKV_FP4_MAX_BLOCKS;
+constexpr int64_t kFp4MaxBlocks = 65536;
 
 struct GatherArgs {
   const uint8_t* kv_cache;

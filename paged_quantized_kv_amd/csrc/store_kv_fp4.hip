@@ -58,10 +58,7 @@ namespace {
 constexpr int kFp4Threads = 256;
 constexpr int kFp4Waves = kFp4Threads / kWave;
 
-#ifndef PKV_FP4_UNROLL
-#define PKV_FP4_UNROLL 2
-#endif
-constexpr int kFp4Unroll = PKV_FP4_UNROLL;  // half-blocks per lane in flight (generic kernel)
+constexpr int kFp4Unroll = 2;  // half-blocks per lane in flight (generic kernel)
 
 constexpr int kFp4Tile = 16;  // tokens per wave item (tile kernel)
 // Items per wave whose loads are in flight together; 2 or 4 cut occupancy
@@ -478,13 +475,10 @@ int launch_generic(const StoreFp4Args& a, hipStream_t stream) {
 
 }  // namespace
 
-#ifndef PKV_FP4_MODE
-#define PKV_FP4_MODE 0  // 0: tile kernel where it applies, 1: always the generic kernel
-#endif
 
 int launch_store_kv_fp4(const StoreFp4Args& a, hipStream_t stream) {
   const bool sides16 = aligned16(a.key_cache) && aligned16(a.value_cache) && a.page_stride % 16 == 0;
-  if (PKV_FP4_MODE == 0 && sides16) {
+  if (sides16) {  // the tile kernel where it applies
     if (a.head_size == 64) return launch_tile<64>(a, stream);
     if (a.head_size == 128) return launch_tile<128>(a, stream);
     if (a.head_size == 256) return launch_tile<256>(a, stream);
