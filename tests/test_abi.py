@@ -333,3 +333,30 @@ def test_binding_rejects_host_tensors():
     x = torch.zeros(4, 128, dtype=torch.uint8)
     with pytest.raises(ValueError, match="device"):
         pkv.pkv_gather_indexer_k_fp8(x, x, x, x, x, block_size=64)
+
+
+def test_last_error_is_per_thread():
+    """pkv_last_error is the calling thread's own message: threads that fail
+    differently (or succeed) at the same time each read back their own."""
+    import threading
+    cases = [(dict(D=100), PKV_EUNSUPPORTED, "multiple of 16"),
+             (dict(R=-1), PKV_EINVAL, "num_reqs"),
+             (dict(T=0), PKV_OK, "")]
+    bad = []
+    start = threading.Barrier(len(cases))
+
+    def worker(kw, code, msg):
+        start.wait()
+        for _ in range(2000):
+            rc = gather(**kw)
+            err = last_error()
+            if rc != code or (msg not in err if msg else err != ""):
+                bad.append((kw, rc, err))
+                return
+
+    threads = [threading.Thread(target=worker, args=c) for c in cases]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad, bad[:3]
