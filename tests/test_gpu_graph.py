@@ -106,3 +106,42 @@ def test_path_captured_in_a_hip_graph():
         torch.cuda.synchronize()
         for i, (t, e) in enumerate(zip(outputs, eager)):
             assert torch.equal(bits(t), e), f"replay {rep}: output {i} differs from the eager run"
+
+
+def test_allocation_free_attention_captured_in_a_hip_graph():
+    """The allocation-free attention (its workspace the library's own device
+    array) captured in a graph; between replays an eager call of the same
+    entry point on another batch rewrites that array.  Every replay must
+    reproduce the eager result bit for bit."""
+    print("\n[case] allocation-free attention in a HIP graph, three replays", flush=True)
+    c = workloads.paged_attention_case(73, 8, 64, 8, lens=[700, 1, 2100, 64, 0, 333, 1024, 5])
+    o = workloads.paged_attention_case(74, 5, 32, 4, lens=[1500, 3, 800, 64, 900])
+    args = []
+    for case in (c, o):
+        S, H, D = case.query.shape
+        args.append(dict(
+            out=torch.empty((S, H, D), dtype=torch.bfloat16, device=DEV),
+            query=dev(case.query.view(np.int16)).view(torch.bfloat16),
+            key_cache=dev(case.key_cache), value_cache=dev(case.value_cache),
+            num_kv_heads=case.num_kv_heads, scale=case.scale,
+            block_tables=dev(case.block_tables), context_lens=dev(case.context_lens),
+            block_size=16, max_context_len=int(case.context_lens.max()),
+            k_scale=case.k_scale, v_scale=case.v_scale, partition_size=256))
+
+    def call(a):
+        pkv.pkv_paged_attention_decode_noalloc(**a)
+
+    call(args[0])
+    torch.cuda.synchronize()
+    eager = bits(args[0]["out"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(args[0])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        args[0]["out"].view(torch.int16).fill_(0x7FC1)
+        call(args[1])                      # another batch through the same array
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(args[0]["out"]), eager), f"replay {rep} differs from the eager run"
