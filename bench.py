@@ -44,7 +44,7 @@ Timing, in this order:
     200 requests with Llama-3.1-70B attention shapes) on its own batch, timed
     the same way;
   - `d2d_copy_same_bytes`: the runtime's device-to-device copy moving the
-    step's bytes (a practical ceiling);
+    step's bytes (a reference point for a plain stream of that size);
   - `cpu_baseline`: the CPU oracle on bounded samples of the same batch, per
     op, on one thread and on every thread used (the oracle's functions called
     on disjoint token or request ranges), median of 5 after one warm-up.
