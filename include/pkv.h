@@ -311,7 +311,7 @@ PKV_API int pkv_gather_kv_fp4_dequant(const void *key_cache, const void *value_c
  *   logits     binary32, row i at logits + i*row_stride, columns
  *              [0, row_cols) of it are written (row_stride >= row_cols).
  *   head_dim   128; num_heads 16, 32, 48 or 64.
- * In this build the entry point validates its arguments and then returns
+ * The entry point currently validates its arguments and then returns
  * PKV_EUNSUPPORTED without launching: a GPU run of its kernel on causal
  * per-request ranges did not finish, and the cause is not found yet.
  */

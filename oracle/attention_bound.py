@@ -2,7 +2,7 @@
 exact (binary64) result, derived from their arithmetic.
 
 TEST INFRASTRUCTURE, like the rest of this package: the tests and
-``__graft_entry__.smoke()`` use it to judge the GPU result; the product
+``__graft_entry__.smoke()`` use it to check the GPU result; the product
 never imports it.
 
 With w_t = exp(l_t - M) the exact softmax weights of the valid tokens,

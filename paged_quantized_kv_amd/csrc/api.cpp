@@ -306,7 +306,7 @@ int pkv_fp8_mqa_logits(const void* q, int64_t q_token_stride, const void* k, con
   // Switched off: a GPU run on causal per-request ranges did not finish, and
   // no cause has been found in the kernel yet; nothing is launched.
   if (!kMqaLogitsEnabled)
-    return fail(PKV_EUNSUPPORTED, "%s: not enabled in this build (a causal-range run of its "
+    return fail(PKV_EUNSUPPORTED, "%s: not enabled (a causal-range run of its "
                 "kernel did not finish; the cause is not found yet)", op);
   pkv::MqaLogitsArgs a{static_cast<const uint8_t*>(q), q_token_stride,
                        static_cast<const uint8_t*>(k), k_scale, weights, ks, ke, logits,

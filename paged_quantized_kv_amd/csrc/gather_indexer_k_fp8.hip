@@ -18,7 +18,7 @@
 //    16-byte loads (kU per lane) and at most 64 tokens, a group is kK runs
 //    with kK * kU = 16 loads per lane, all in flight before the first store:
 //    16 KB per wave for 64 x 128-byte runs.  On the 256 x 1000-token batch
-//    (interleaved runs on one box, kernel trace) one 8 KB run per wave took
+//    (interleaved runs on one GPU, kernel trace) one 8 KB run per wave took
 //    12.3 us, two per wave 11.0-11.5 us, four per wave 12.7 us, and two per
 //    wave copied one after the other 14.0 us.  Other shapes: one run per
 //    wave, a generic loop;
@@ -116,7 +116,7 @@ __device__ __forceinline__ int32_t wave_id_uniform() {
 // past a short run's end re-read its last chunk and empty runs re-read the
 // first chunk of page 0; they are not stored.  Three details of this shape
 // were each measured on the 256 x 1000-token batch (interleaved runs on one
-// box): loads issued as flat instructions (the compiler emits them for the
+// GPU): loads issued as flat instructions (the compiler emits them for the
 // selected source pointers) ran 6-8% faster than the same loads as global
 // instructions; waiting for every load before the first store beat storing
 // each chunk as its load returned; and the same steps spread over helper
