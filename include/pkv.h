@@ -128,7 +128,10 @@ PKV_API const char *pkv_last_error(void);
  *   cu_seq_lens        int32 [num_reqs + 1]; cu_seq_lens[0] need not be 0.
  *   head_dim           multiple of 16.
  * Errors: PKV_EINVAL for negative sizes or missing pointers, PKV_EALIGN,
- * PKV_EUNSUPPORTED when head_dim % 16 != 0 or the stride is too small.
+ * PKV_EUNSUPPORTED when head_dim % 16 != 0, the stride is too small,
+ * num_reqs * max_blocks_per_req exceeds 2^31 - 1 or max_blocks_per_req
+ * exceeds 2^22.  Tables of more than 2^22 entries are gathered by several
+ * launches (request ranges), in order on the stream.
  */
 PKV_API int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_scale,
                                      const int32_t *block_table, const int32_t *cu_seq_lens,
@@ -157,6 +160,8 @@ PKV_API int pkv_gather_indexer_k_fp8(const void *kv_cache, void *k_fp8, void *k_
  *   slot_mapping  int64 [num_tokens]; 8-byte aligned.
  *   kv_cache      written; 16-byte aligned; stride as for the gather.
  *   head_dim      multiple of 16, at most 1024.
+ * Calls of more than 2^22 tokens are stored by several launches (token
+ * ranges), in order on the stream.
  */
 PKV_API int pkv_store_indexer_k_fp8(const void *k, int64_t k_row_stride, int32_t k_dtype,
                                     const int64_t *slot_mapping, int64_t num_tokens,

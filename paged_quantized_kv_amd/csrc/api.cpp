@@ -90,17 +90,29 @@ int pkv_gather_indexer_k_fp8(const void* kv_cache, void* k_fp8, void* k_scale,
   if (num_reqs == 0 || num_tokens == 0 || max_blocks_per_req == 0) return ok();
   if ((int64_t)num_reqs * max_blocks_per_req > INT32_MAX)
     return fail(PKV_EUNSUPPORTED, "%s: num_reqs * max_blocks_per_req exceeds 2^31-1", op);
+  if (max_blocks_per_req > pkv::kGatherMaxEntriesPerLaunch)
+    return fail(PKV_EUNSUPPORTED, "%s: max_blocks_per_req must be <= %lld, got %d", op,
+                (long long)pkv::kGatherMaxEntriesPerLaunch, max_blocks_per_req);
   if (!kv_cache || !k_fp8 || !k_scale || !block_table || !cu_seq_lens)
     return fail(PKV_EINVAL, "%s: null buffer pointer", op);
   if (!aligned(kv_cache, 16) || !aligned(k_fp8, 16))
     return fail(PKV_EALIGN, "%s: kv_cache and k_fp8 must be 16-byte aligned", op);
   if (!aligned(k_scale, 4) || !aligned(block_table, 4) || !aligned(cu_seq_lens, 4))
     return fail(PKV_EALIGN, "%s: k_scale, block_table and cu_seq_lens must be 4-byte aligned", op);
-  pkv::GatherArgs a{static_cast<const uint8_t*>(kv_cache), static_cast<uint8_t*>(k_fp8),
-                    static_cast<uint8_t*>(k_scale), block_table, cu_seq_lens, num_reqs,
-                    max_blocks_per_req, num_tokens, num_blocks, cache_block_stride, block_size,
-                    head_dim};
-  return launched(pkv::launch_gather_indexer_k_fp8(a, static_cast<hipStream_t>(stream)), op);
+  // request chunks of at most kGatherMaxEntriesPerLaunch table entries; the
+  // rows a chunk writes come from its own cu_seq_lens entries
+  const int64_t per_launch = pkv::kGatherMaxEntriesPerLaunch / max_blocks_per_req;
+  for (int64_t r0 = 0; r0 < num_reqs; r0 += per_launch) {
+    const int64_t left = num_reqs - r0;
+    pkv::GatherArgs a{static_cast<const uint8_t*>(kv_cache), static_cast<uint8_t*>(k_fp8),
+                      static_cast<uint8_t*>(k_scale), block_table + r0 * max_blocks_per_req,
+                      cu_seq_lens + r0, (int32_t)(left < per_launch ? left : per_launch),
+                      max_blocks_per_req, num_tokens, num_blocks, cache_block_stride,
+                      block_size, head_dim};
+    if (int e = pkv::launch_gather_indexer_k_fp8(a, static_cast<hipStream_t>(stream)))
+      return launched(e, op);
+  }
+  return ok();
 }
 
 int pkv_store_indexer_k_fp8(const void* k, int64_t k_row_stride, int32_t k_dtype,
@@ -124,10 +136,19 @@ int pkv_store_indexer_k_fp8(const void* k, int64_t k_row_stride, int32_t k_dtype
     return fail(PKV_EALIGN, "%s: k and kv_cache must be 16-byte aligned", op);
   if (!aligned(slot_mapping, 8)) return fail(PKV_EALIGN, "%s: slot_mapping must be 8-byte aligned", op);
   if (num_tokens > ((int64_t)1 << 40)) return fail(PKV_EUNSUPPORTED, "%s: num_tokens too large", op);
-  pkv::StoreFp8Args a{static_cast<const uint16_t*>(k), k_row_stride, k_dtype, slot_mapping, num_tokens,
-                      static_cast<uint8_t*>(kv_cache), num_blocks, cache_block_stride, block_size,
-                      log2_or_neg(block_size), head_dim};
-  return launched(pkv::launch_store_indexer_k_fp8(a, static_cast<hipStream_t>(stream)), op);
+  // token chunks of at most kStoreFp8MaxTokensPerLaunch
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  for (int64_t t0 = 0; t0 < num_tokens; t0 += pkv::kStoreFp8MaxTokensPerLaunch) {
+    const int64_t left = num_tokens - t0;
+    pkv::StoreFp8Args a{k16 + t0 * k_row_stride, k_row_stride, k_dtype, slot_mapping + t0,
+                        left < pkv::kStoreFp8MaxTokensPerLaunch ? left
+                                                                : pkv::kStoreFp8MaxTokensPerLaunch,
+                        static_cast<uint8_t*>(kv_cache), num_blocks, cache_block_stride,
+                        block_size, log2_or_neg(block_size), head_dim};
+    if (int e = pkv::launch_store_indexer_k_fp8(a, static_cast<hipStream_t>(stream)))
+      return launched(e, op);
+  }
+  return ok();
 }
 
 int pkv_store_kv_fp4(const void* key, int64_t key_row_stride, const void* value,

@@ -16,6 +16,13 @@ constexpr int64_t kGatherMaxReqsPerLaunch = 16000;
 // read-backs, the NVFP4 store): larger inputs loop.
 constexpr int64_t kGatherMaxBlocks = 65536;
 constexpr int64_t kFp4MaxBlocks = 65536;
+// The fp8 store and the dense-table gather are one-pass kernels whose grid
+// follows the input, and a launch must stay below 2^32 work-items: the C ABI
+// splits larger calls into launches of at most this many tokens (store) or
+// block-table entries (gather), enqueued in order on the caller's stream.
+// Tokens and requests are independent, so the split changes no result.
+constexpr int64_t kStoreFp8MaxTokensPerLaunch = int64_t{1} << 22;
+constexpr int64_t kGatherMaxEntriesPerLaunch = int64_t{1} << 22;
 
 struct GatherArgs {
   const uint8_t* kv_cache;

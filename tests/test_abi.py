@@ -78,6 +78,7 @@ def gather(**kw):
     (dict(kv_cache=A + 4), PKV_EALIGN, "16-byte"),
     (dict(k_scale=A + 2), PKV_EALIGN, "4-byte"),
     (dict(R=70000, maxb=40000), PKV_EUNSUPPORTED, "2^31"),
+    (dict(R=1, maxb=(1 << 22) + 1), PKV_EUNSUPPORTED, "max_blocks_per_req must be <="),
 ])
 def test_gather_validation(kw, code, msg):
     assert gather(**kw) == code
