@@ -36,14 +36,8 @@ namespace {
 
 constexpr int kDqThreads = 256;
 constexpr int kDqWaves = kDqThreads / kWave;
-#ifndef PKV_IDX_DQ_UNROLL
-#define PKV_IDX_DQ_UNROLL 4
-#endif
-#ifndef PKV_FP4_DQ_UNROLL
-#define PKV_FP4_DQ_UNROLL 32
-#endif
-constexpr int kIdxUnroll = PKV_IDX_DQ_UNROLL;  // lane units (8 elements each) in flight, indexer
-constexpr int kFp4Unroll = PKV_FP4_DQ_UNROLL;  // lane units in flight, NVFP4
+constexpr int kIdxUnroll = 4;   // lane units (8 elements each) in flight, indexer
+constexpr int kFp4Unroll = 32;  // lane units in flight, NVFP4 (direct kernel)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
