@@ -175,6 +175,22 @@ def test_one_long_context_across_many_units():
     print(f"max err / bound = {worst:.3g}", flush=True)
 
 
+def test_one_64k_context_both_splits():
+    """A 64K-token context beside a short and a one-token one.  At P=256 the
+    balanced split spreads the long sequence over about 340 units (the reduce
+    combines that many partials per head); at P=2048 the fixed split gives it
+    32 partitions."""
+    lens = [65536, 777, 1]
+    assert balanced_units(3, 64, 8, max(lens), 256, 3072) > 300
+    assert balanced_units(3, 64, 8, max(lens), 2048, 3072) == 0
+    banner("paged attention one 64K-token context, P=256 and P=2048")
+    c = workloads.paged_attention_case(93, len(lens), 64, 8, lens=lens)
+    ref, b = reference(c)
+    for P in (256, 2048):
+        worst = check(run(c, P), ref, b)
+        print(f"P={P}: max err / bound = {worst:.3g}", flush=True)
+
+
 @pytest.mark.parametrize("S,balanced", [(4096, True), (4100, False)])
 def test_many_sequences(S, balanced):
     """The most sequences the balanced split takes (their block counts fill
