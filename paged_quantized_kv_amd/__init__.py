@@ -130,6 +130,13 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
     return t
 
 
+def _row_stride(t: torch.Tensor, natural: int) -> int:
+    """stride(0) of a row-major view; an empty tensor's strides carry no
+    layout (torch and numpy give empty arrays arbitrary strides), so it gets
+    the natural one."""
+    return t.stride(0) if t.numel() else natural
+
+
 def _src_dtype(t: torch.Tensor, name: str) -> int:
     if t.dtype == torch.bfloat16:
         return DTYPE_BF16
@@ -201,7 +208,7 @@ def pkv_store_indexer_k_fp8(k, slot_mapping, kv_cache, block_size: int | None = 
     _dev(slot_mapping, "slot_mapping", torch.int64)
     _dev(kv_cache, "kv_cache", torch.uint8)
     _contig(slot_mapping, "slot_mapping")
-    if k.dim() != 2 or k.stride(1) != 1:
+    if k.dim() != 2 or (k.numel() and k.stride(1) != 1):
         raise ValueError("k must be [num_tokens, head_dim] with unit element stride")
     num_tokens, head_dim = k.shape
     if slot_mapping.numel() != num_tokens:
@@ -213,7 +220,8 @@ def pkv_store_indexer_k_fp8(k, slot_mapping, kv_cache, block_size: int | None = 
     if kv_cache.stride(-1) != 1:
         raise ValueError("kv_cache pages must be contiguous")
     _check(_lib.pkv_store_indexer_k_fp8(
-        k.data_ptr(), k.stride(0), k_dtype, slot_mapping.data_ptr(), num_tokens, kv_cache.data_ptr(),
+        k.data_ptr(), _row_stride(k, head_dim), k_dtype, slot_mapping.data_ptr(), num_tokens,
+        kv_cache.data_ptr(),
         kv_cache.shape[0], kv_cache.stride(0), block_size, head_dim, _stream(stream)))
 
 
@@ -242,7 +250,7 @@ def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, 
         raise ValueError("key and value must both be [num_tokens, num_heads, head_size]")
     num_tokens, num_heads, head_size = key.shape
     for t, n in ((key, "key"), (value, "value")):
-        if t.stride(2) != 1 or t.stride(1) != head_size:
+        if t.numel() and (t.stride(2) != 1 or t.stride(1) != head_size):
             raise ValueError(f"{n}: heads and elements must be contiguous (only stride(0) is free)")
     if slot_mapping.numel() != num_tokens:
         raise ValueError("slot_mapping must have num_tokens entries")
@@ -261,7 +269,8 @@ def pkv_store_kv_fp4(key, value, key_cache, value_cache, slot_mapping, k_scale, 
     if key_cache.stride(0) != value_cache.stride(0) or key_cache.shape[0] != value_cache.shape[0]:
         raise ValueError("key_cache and value_cache must share num_blocks and page stride")
     _check(_lib.pkv_store_kv_fp4(
-        key.data_ptr(), key.stride(0), value.data_ptr(), value.stride(0), src_dtype,
+        key.data_ptr(), _row_stride(key, num_heads * head_size), value.data_ptr(),
+        _row_stride(value, num_heads * head_size), src_dtype,
         key_cache.data_ptr(),
         value_cache.data_ptr(), slot_mapping.data_ptr(), num_tokens, num_heads, head_size,
         block_size, key_cache.shape[0], key_cache.stride(0), layout, k_scale.data_ptr(),
@@ -293,7 +302,7 @@ def pkv_gather_indexer_k_dequant(kv_cache, out, block_table, cu_seq_lens,
     _dev(kv_cache, "kv_cache", torch.uint8)
     _dev(out, "out")
     out_dtype = _src_dtype(out, "out")
-    if out.dim() != 2 or out.stride(1) != 1:
+    if out.dim() != 2 or (out.numel() and out.stride(1) != 1):
         raise ValueError("out must be [num_tokens, head_dim] with contiguous rows")
     num_tokens, head_dim = out.shape
     num_reqs, max_blocks = _table_args(block_table, cu_seq_lens)
@@ -304,7 +313,8 @@ def pkv_gather_indexer_k_dequant(kv_cache, out, block_table, cu_seq_lens,
     if kv_cache.dim() >= 2 and kv_cache.stride(-1) != 1:
         raise ValueError("kv_cache pages must be contiguous")
     _check(_lib.pkv_gather_indexer_k_dequant(
-        kv_cache.data_ptr(), out.data_ptr(), out.stride(0), out_dtype, block_table.data_ptr(),
+        kv_cache.data_ptr(), out.data_ptr(), _row_stride(out, head_dim), out_dtype,
+        block_table.data_ptr(),
         cu_seq_lens.data_ptr(), num_reqs, max_blocks, num_tokens, kv_cache.shape[0],
         kv_cache.stride(0), block_size, head_dim, _stream(stream)))
 
@@ -333,7 +343,7 @@ def pkv_gather_kv_fp4_dequant(key_cache, value_cache, key_out, value_out, block_
         raise ValueError("key_out and value_out must both be [num_tokens, num_heads, head_size]")
     num_tokens, num_heads, head_size = key_out.shape
     for t, n in ((key_out, "key_out"), (value_out, "value_out")):
-        if t.stride(2) != 1 or t.stride(1) != head_size:
+        if t.numel() and (t.stride(2) != 1 or t.stride(1) != head_size):
             raise ValueError(f"{n}: heads and elements must be contiguous (only stride(0) is free)")
     if k_scale.numel() != 1 or v_scale.numel() != 1:
         raise ValueError("k_scale and v_scale must be scalars")
@@ -351,8 +361,9 @@ def pkv_gather_kv_fp4_dequant(key_cache, value_cache, key_out, value_out, block_
     if key_cache.stride(0) != value_cache.stride(0) or key_cache.shape[0] != value_cache.shape[0]:
         raise ValueError("key_cache and value_cache must share num_blocks and page stride")
     _check(_lib.pkv_gather_kv_fp4_dequant(
-        key_cache.data_ptr(), value_cache.data_ptr(), key_out.data_ptr(), key_out.stride(0),
-        value_out.data_ptr(), value_out.stride(0), out_dtype, block_table.data_ptr(),
+        key_cache.data_ptr(), value_cache.data_ptr(), key_out.data_ptr(),
+        _row_stride(key_out, num_heads * head_size), value_out.data_ptr(),
+        _row_stride(value_out, num_heads * head_size), out_dtype, block_table.data_ptr(),
         cu_seq_lens.data_ptr(), num_reqs, max_blocks, num_tokens, num_heads, head_size,
         block_size, key_cache.shape[0], key_cache.stride(0), layout, k_scale.data_ptr(),
         v_scale.data_ptr(), _stream(stream)))
@@ -409,7 +420,7 @@ def pkv_fp8_mqa_logits(q, k, k_scale, weights, ks, ke, logits, stream=None):
     _dev(logits, "logits", torch.float32)
     for t, n in ((k, "k"), (k_scale, "k_scale"), (weights, "weights"), (ks, "ks"), (ke, "ke")):
         _contig(t, n)
-    if q.dim() != 3 or q.stride(2) != 1 or q.stride(1) != q.shape[2]:
+    if q.dim() != 3 or (q.numel() and (q.stride(2) != 1 or q.stride(1) != q.shape[2])):
         raise ValueError("q must be [num_q, num_heads, head_dim] with contiguous heads")
     num_q, num_heads, head_dim = q.shape
     if k.dim() != 2 or k.shape[1] != head_dim:
@@ -425,11 +436,12 @@ def pkv_fp8_mqa_logits(q, k, k_scale, weights, ks, ke, logits, stream=None):
         raise ValueError("weights must be [num_q, num_heads]")
     if ks.numel() != num_q or ke.numel() != num_q:
         raise ValueError("ks and ke must have num_q entries")
-    if logits.dim() != 2 or logits.shape[0] != num_q or logits.stride(1) != 1:
+    if logits.dim() != 2 or logits.shape[0] != num_q or (logits.numel() and logits.stride(1) != 1):
         raise ValueError("logits must be [num_q, row_cols] with contiguous rows")
     _check(_lib.pkv_fp8_mqa_logits(
-        q.data_ptr(), q.stride(0) * q.element_size(), k.data_ptr(), k_scale.data_ptr(),
-        weights.data_ptr(), ks.data_ptr(), ke.data_ptr(), logits.data_ptr(), logits.stride(0),
+        q.data_ptr(), _row_stride(q, num_heads * head_dim) * q.element_size(), k.data_ptr(),
+        k_scale.data_ptr(), weights.data_ptr(), ks.data_ptr(), ke.data_ptr(), logits.data_ptr(),
+        _row_stride(logits, logits.shape[1]),
         logits.shape[1], num_q, num_heads, num_k, head_dim, _stream(stream)))
 
 

@@ -119,6 +119,32 @@ def test_gather_empty():
                                  dev(w.block_table), dev(w.cu_seq_lens), block_size=64)
 
 
+def test_empty_inputs_of_every_store_and_read_back():
+    """Zero tokens, in tensors whose strides are those numpy and torch give
+    empty arrays (here all zero): every entry point accepts them, launches
+    nothing and leaves the caches as they were."""
+    banner("empty inputs, zero strides")
+    w = workloads.c1_tiny_gather()
+    cache = dev(w.cache_init)
+    empty_k = torch.from_numpy(np.zeros((0, 128), np.int16)).to(DEV).view(torch.bfloat16)
+    empty_k = empty_k.as_strided((0, 128), (0, 0))
+    pkv.pkv_store_indexer_k_fp8(empty_k, dev(np.zeros(0, np.int64)), cache, block_size=64)
+    out = torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV).as_strided((0, 128), (0, 0))
+    pkv.pkv_gather_indexer_k_dequant(cache, out, dev(w.block_table), dev(w.cu_seq_lens),
+                                     block_size=64)
+    f = workloads.small_fp4(11, 8, H=2, D=128, B=16)
+    c4 = dev(f.cache_init)
+    e3 = torch.zeros((0, 2, 128), dtype=torch.bfloat16, device=DEV).as_strided((0, 2, 128),
+                                                                               (0, 0, 0))
+    one = torch.ones(1, dtype=torch.float32, device=DEV)
+    pkv.pkv_store_kv_fp4(e3, e3, c4[:, 0], c4[:, 1], dev(np.zeros(0, np.int64)), one, one,
+                         block_size=16, layout=0)
+    pkv.pkv_gather_kv_fp4_dequant(c4[:, 0], c4[:, 1], e3, e3, dev(np.zeros((1, 1), np.int32)),
+                                  dev(np.zeros(2, np.int32)), one, one, block_size=16, layout=0)
+    np.testing.assert_array_equal(host(cache), w.cache_init)
+    np.testing.assert_array_equal(host(c4), f.cache_init)
+
+
 # ---------------------------------------------------------------- fp8 store
 def run_store8(w, k_bits=None, slots=None, cache_np=None, row_pad=0):
     kb = w.k_bits if k_bits is None else k_bits
