@@ -18,7 +18,6 @@ import os
 import subprocess
 import tempfile
 
-import pytest
 
 SRC = r"""
 #include <math.h>
