@@ -404,7 +404,8 @@ PKV_API int pkv_paged_attention_decode(void *out, float *exp_sums, float *max_lo
  * num_heads * ceil(max_context_len / partition_size) (head_size 128); one
  * that needs more than PKV_ATTENTION_SCRATCH_BYTES returns PKV_EUNSUPPORTED
  * and enqueues nothing (PKV_ELAUNCH if the array's address cannot be looked
- * up).  Every workspace element a call reads was written earlier in the
+ * up).  The array is the current device's, so `stream` must belong to the
+ * current device (PKV_EINVAL otherwise).  Every workspace element a call reads was written earlier in the
  * same call, so nothing carries over from one call to the next.  All calls
  * on one GPU share its array: calls that may run at the same time on one
  * GPU (on different streams, or enqueued from different threads without

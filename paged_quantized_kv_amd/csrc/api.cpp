@@ -451,6 +451,15 @@ int pkv_paged_attention_decode_noalloc(void* out, const void* query, const void*
                 "%s: the call needs %lld bytes of workspace, more than the %lld-byte built-in "
                 "scratch (use pkv_paged_attention_decode with a caller workspace)",
                 op, (long long)need, (long long)PKV_ATTENTION_SCRATCH_BYTES);
+  // the scratch address is looked up for the current device, so the stream
+  // must belong to that device (host queries only: nothing is enqueued)
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess ||
+      hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess)
+    return fail(PKV_ELAUNCH, "%s: querying the current device or the stream's device failed", op);
+  if (sdev != cur)
+    return fail(PKV_EINVAL, "%s: the stream belongs to device %d but device %d is current", op,
+                sdev, cur);
   void* base = nullptr;
   if (int e = pkv::attention_scratch(&base))
     return fail(PKV_ELAUNCH, "%s: looking up the scratch array failed: %s", op,
