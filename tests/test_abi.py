@@ -361,3 +361,23 @@ def test_last_error_is_per_thread():
     for t in threads:
         t.join()
     assert not bad, bad[:3]
+
+
+def test_plain_c_client_builds_and_links(tmp_path):
+    """pkv.h compiles as strict C99 (gcc -pedantic -Werror) and a C program
+    linked against libpkv.so gets the documented status codes and messages
+    (host checks only: no GPU is touched)."""
+    import shutil
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    exe = tmp_path / "pkv_c_client"
+    libdir = os.path.dirname(pkv.library_path())
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c_client", "pkv_c_client.c"),
+                        "-o", str(exe), os.path.join(libdir, "libpkv.so"),
+                        "-Wl,-rpath," + libdir], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "c client ok" in r.stdout, (r.returncode, r.stderr[-2000:])
