@@ -4,6 +4,7 @@ include/pkv.h declares, and its host-side validation rejects bad arguments
 import ctypes
 import os
 import re
+import shutil
 import subprocess
 
 import pytest
@@ -367,7 +368,6 @@ def test_plain_c_client_builds_and_links(tmp_path):
     """pkv.h compiles as strict C99 (gcc -pedantic -Werror) and a C program
     linked against libpkv.so gets the documented status codes and messages
     (host checks only: no GPU is touched)."""
-    import shutil
     gcc = shutil.which("gcc")
     if gcc is None:
         pytest.skip("gcc not available")
@@ -381,3 +381,29 @@ def test_plain_c_client_builds_and_links(tmp_path):
     assert r.returncode == 0, r.stderr[-3000:]
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "c client ok" in r.stdout, (r.returncode, r.stderr[-2000:])
+
+
+def build_hip_client(tmp_path):
+    """Builds tests/c_client/pkv_hip_client.cpp (host code only) with g++
+    against the HIP runtime and libpkv.so; returns the executable's path."""
+    gxx = shutil.which("g++")
+    if gxx is None or not os.path.exists("/opt/rocm/include/hip/hip_runtime_api.h"):
+        pytest.skip("g++ or the HIP headers not available")
+    exe = tmp_path / "pkv_hip_client"
+    libdir = os.path.dirname(pkv.library_path())
+    r = subprocess.run([gxx, "-std=c++17", "-O1", "-Wall", "-Wextra", "-Werror",
+                        "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        "-I", os.path.join(ROOT, "include"),
+                        os.path.join(ROOT, "tests", "c_client", "pkv_hip_client.cpp"),
+                        "-o", str(exe), os.path.join(libdir, "libpkv.so"),
+                        "-L/opt/rocm/lib", "-lamdhip64",
+                        "-Wl,-rpath," + libdir + ":/opt/rocm/lib"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    return exe
+
+
+def test_hip_client_builds(tmp_path):
+    """The C++ client that drives libpkv with raw HIP buffers and its own
+    stream compiles warning-free against pkv.h (it runs in the GPU tests)."""
+    assert build_hip_client(tmp_path).exists()
