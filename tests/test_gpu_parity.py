@@ -196,6 +196,72 @@ def test_store_fp8_row_stride_and_skips():
     run_store8(w, slots=np.full_like(sl, -1))
 
 
+def test_stores_confine_non_finite_tokens_to_their_own_bytes():
+    """Non-finite source values are outside the contract (their codes are
+    unspecified), but memory access is not: tokens with NaN or infinite
+    elements may write only their own code row and scale bytes (fp8 store)
+    or their own data and block-scale bytes (NVFP4 store); every other byte
+    must be the oracle's.  The bytes a token owns are found by storing the
+    non-finite tokens alone into a cache and into its bitwise complement:
+    a byte they write differs from at least one of the two."""
+    banner("stores with non-finite tokens")
+    g = workloads.rng(321)
+    bad_tok = np.array([0, 5, 63, 64, 200, 511])
+
+    # fp8 indexer store
+    w = workloads.small_indexer(31, [512], drop_frac=0.0)
+    x = g.standard_normal((512, 128)).astype(np.float32)
+    x[0, 3] = np.nan
+    x[5, :] = np.inf
+    x[63, 100] = -np.inf
+    x[64, ::7] = np.nan
+    x[200, 0] = np.inf
+    x[511] = np.nan
+    kb = workloads.bf16_bits(x)
+    ref = w.cache_init.copy()
+    oracle.store_indexer_k_fp8(kb, w.slot_mapping, ref, 64, 128)
+    cache = dev(w.cache_init)
+    pkv.pkv_store_indexer_k_fp8(bf16_dev(kb), dev(w.slot_mapping), cache, block_size=64)
+    got = host(cache)
+    only = np.full(512, -1, np.int64)
+    only[bad_tok] = w.slot_mapping[bad_tok]
+    owned = np.zeros(w.cache_init.shape, bool)
+    for init in (w.cache_init, ~w.cache_init):
+        o = init.copy()
+        oracle.store_indexer_k_fp8(kb, only, o, 64, 128)
+        owned |= o != init
+    assert owned.sum() == len(bad_tok) * (128 + 4)
+    np.testing.assert_array_equal(got[~owned], ref[~owned])
+
+    # NVFP4 store: NaN / inf in some 16-element blocks of some tokens
+    f = workloads.paged_fp4(33, [100, 37, 64], H=4, D=128, B=16, drop_frac=0.0)
+    T = f.num_tokens
+    kf = f.key_bits.copy()
+    vf = f.value_bits.copy()
+    bad4 = np.array([0, 17, 99, 100, 136, T - 1])
+    kf[bad4[:3], 5] = 0x7FC0                         # NaN in one block
+    vf[bad4[3:], :] = 0x7F80                         # +inf everywhere
+    ref4 = f.cache_init.copy()
+    oracle.store_kv_fp4(kf, vf, ref4, f.slot_mapping, 4, 128, 16, 0, f.k_scale, f.v_scale)
+    c4 = dev(f.cache_init)
+    shape = (T, 4, 128)
+    pkv.pkv_store_kv_fp4(bf16_dev(kf, shape), bf16_dev(vf, shape), c4[:, 0], c4[:, 1],
+                         dev(f.slot_mapping),
+                         torch.tensor([f.k_scale], dtype=torch.float32, device=DEV),
+                         torch.tensor([f.v_scale], dtype=torch.float32, device=DEV),
+                         block_size=16, layout=0)
+    got4 = host(c4)
+    only4 = np.full(T, -1, np.int64)
+    only4[bad4] = f.slot_mapping[bad4]
+    owned4 = np.zeros(f.cache_init.shape, bool)
+    for init in (f.cache_init, ~f.cache_init):
+        o = init.copy()
+        oracle.store_kv_fp4(kf, vf, o, only4, 4, 128, 16, 0, f.k_scale, f.v_scale)
+        owned4 |= o != init
+    assert owned4.sum() == len(bad4) * 2 * 4 * (64 + 8)
+    np.testing.assert_array_equal(got4[~owned4], ref4[~owned4])
+
+
 def test_store_fp8_value_edge_cases():
     """Zero, tiny (IEEE-division path), subnormal, huge and tie-making tokens."""
     banner("store fp8 value edge cases")
