@@ -88,3 +88,44 @@ def test_repeated_calls_are_bit_identical():
             print(f"{i + 1} calls: identical", flush=True)
     torch.cuda.synchronize()
     assert int(bad) == 0
+
+
+def test_bench_step_repeats_bit_identically():
+    """The benchmark's step -- fp8 store, NVFP4 store, gather over the 256 x
+    1000-token batch -- repeated 500 times over one buffer set gives the
+    same bytes every time (the first step's, which the parity tests compare
+    with the oracle)."""
+    print("\n[case] soak: 500 steps of the 256 x 1000-token batch", flush=True)
+    w = workloads.c2_prefill_256x1000()
+    f = workloads.prefill_fp4()
+    T = w.num_tokens
+    k = dev(w.k_bits.view(np.int16)).view(torch.bfloat16)
+    sl, cache = dev(w.slot_mapping), dev(w.cache_init)
+    kf, ks = dev(w.k_fp8_init[:T]), dev(w.k_scale_init[:T])
+    bt, cu = dev(w.block_table), dev(w.cu_seq_lens)
+    key = dev(f.key_bits.view(np.int16)).view(torch.bfloat16).view(T, 8, 128)
+    val = dev(f.value_bits.view(np.int16)).view(torch.bfloat16).view(T, 8, 128)
+    sl4, c4 = dev(f.slot_mapping), dev(f.cache_init)
+    k4s = torch.tensor([f.k_scale], dtype=torch.float32, device=DEV)
+    v4s = torch.tensor([f.v_scale], dtype=torch.float32, device=DEV)
+
+    def step():
+        pkv.pkv_store_indexer_k_fp8(k, sl, cache, block_size=64)
+        pkv.pkv_store_kv_fp4(key, val, c4[:, 0], c4[:, 1], sl4, k4s, v4s, block_size=16,
+                             layout=0)
+        pkv.pkv_gather_indexer_k_fp8(cache, kf, ks, bt, cu, block_size=64)
+
+    step()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in (cache, c4, kf, ks)]
+    bad = torch.zeros((), dtype=torch.int64, device=DEV)
+    for i in range(500):
+        # the outputs are rewritten with the same bytes: clear the gather's
+        # outputs first so that a skipped write would show
+        kf.zero_()
+        ks.zero_()
+        step()
+        for t, r in zip((cache, c4, kf, ks), refs):
+            bad += (t != r).any().to(torch.int64)
+    torch.cuda.synchronize()
+    assert int(bad) == 0
