@@ -331,7 +331,9 @@ PKV_API int pkv_fp8_mqa_logits(const void *q, int64_t q_token_stride, const void
  * Attention kernels": the op paged_attention(out, exp_sums, max_logits,
  * tmp_out, query, key_cache, value_cache, num_kv_heads, scale, block_tables,
  * context_lens, block_size, max_context_len, ..., kv_cache_dtype, k_scale,
- * v_scale, ..., partition_size), with an fp8 cache and per-tensor scales).
+ * v_scale, ..., partition_size), with an fp8 cache and per-tensor scales;
+ * the schema's optional ALiBi slopes and fp8 output scale are not taken:
+ * no ALiBi, bf16 output).
  *
  * For sequence s < num_seqs and head h < num_heads, with
  * kvh = h / (num_heads / num_kv_heads) and tokens t < context_lens[s]:
